@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+None of these re-types the oracle's own formulas: each compares the oracle with
+a closed form derived separately (kept-pair counts, Q = 0 / constant-V results,
+the permutation's defining properties), with numbers the pages print (the kept
+density), with hand-worked examples stored under tests/golden/, with a library
+routine (torch's fp64 scaled_dot_product_attention), with pure-Python brute
+force, or with an independent geometric derivation of the tile classes.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Geometry
+import svattn_synth as synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms for kept pairs.
+#
+# Spatial head, window w (w <= F-1): a query in frame f keeps the frames of
+# [max(0, f-w), min(F-1, f+w)], plus frame 0 when f - w > 0.  Summing the
+# clipped window over f gives F(2w+1) - w(w+1) frame pairs, and frame 0 is
+# added for the F-1-w frames f >= w+1; every frame pair contributes P*P.
+#
+# Temporal head, radius r: frame-0 keys always count (F * P * P pairs); for
+# keys in frames 1..F-1 a query patch (y, x) keeps R_H(y) * R_W(x) patches per
+# frame with R_L(c) = min(L-1, c+r) - max(0, c-r) + 1, and sum_c R_L(c) =
+# L(2r+1) - r(r+1) for r <= L-1 (else L*L).
+# ---------------------------------------------------------------------------
+
+def _closed_spatial(F, H, W, w):
+    P = H * W
+    if w >= F - 1:
+        return (F * P) ** 2
+    return P * P * (F * (2 * w + 1) - w * (w + 1) + max(0, F - 1 - w))
+
+
+def _sum_window(L, r):
+    return L * L if r >= L - 1 else L * (2 * r + 1) - r * (r + 1)
+
+
+def _closed_temporal(F, H, W, r):
+    P = H * W
+    return F * (F - 1) * _sum_window(H, r) * _sum_window(W, r) + F * P * P
+
+
+def _row_closed_temporal(F, H, W, r, t):
+    P = H * W
+    y, x = (t % P) // W, (t % P) % W
+    ry = min(H - 1, y + r) - max(0, y - r) + 1
+    rx = min(W - 1, x + r) - max(0, x - r) + 1
+    return P + (F - 1) * ry * rx
+
+
+def _row_closed_spatial(F, H, W, w, t):
+    P = H * W
+    f = t // P
+    lo, hi = max(0, f - w), min(F - 1, f + w)
+    return P * ((hi - lo + 1) + (1 if lo > 0 else 0))
+
+
+@pytest.mark.parametrize("F,H,W,w,r", [
+    (4, 8, 8, 1, 1),      # tiny workload
+    (5, 24, 40, 1, 2),    # small workload
+    (6, 5, 7, 2, 3),      # clipped windows on a non-square grid
+    (3, 4, 9, 0, 0),      # degenerate: own frame / own patch only
+    (3, 4, 4, 2, 3),      # windows cover everything -> dense
+])
+def test_kept_count_closed_form(F, H, W, w, r):
+    g = Geometry(F, H, W)
+    assert oracle.kept_count(g, "spatial", w, 0) == _closed_spatial(F, H, W, w)
+    assert oracle.kept_count(g, "temporal", 0, r) == _closed_temporal(F, H, W, r)
+    assert oracle.kept_count(g, "dense", 0, 0) == g.n ** 2
+
+
+def test_tiny_and_small_kept_totals():
+    # Tiny: spatial 49,152 and temporal 22,192 of 65,536 pairs (75.00% / 33.86%).
+    assert _closed_spatial(4, 8, 8, 1) == 49152
+    assert _closed_temporal(4, 8, 8, 1) == 22192
+
+
+def test_headline_density_matches_pages():
+    """The pages print ~38.87% kept pairs at 75,600 tokens x 10 heads; the
+    mask parameters (w=1 on 5 spatial heads, r=31 on 5 temporal heads) are the
+    reading chosen to meet it."""
+    pages = _golden("pages_numbers.json")
+    target = pages["kept_fraction_percent"]["value"]
+    wl = synth.WORKLOADS["headline"]
+    F, H, W = wl.frames, wl.height, wl.width
+    N = F * H * W
+    assert N == pages["workload"]["tokens"] and wl.n_heads == pages["workload"]["heads"]
+    kept = sum(_closed_spatial(F, H, W, h.window) if h.kind == "spatial"
+               else _closed_temporal(F, H, W, h.radius) for h in wl.heads)
+    pct = 100.0 * kept / (wl.n_heads * N * N)
+    assert abs(pct - target) < 0.01, pct
+    # the oracle's brute-force per-row counts agree with the per-row closed form
+    g = Geometry(F, H, W)
+    rows = synth.sample_rows(wl, 64)[0]
+    got_s = oracle.kept_counts_per_row(g, "spatial", 1, 0, rows)
+    got_t = oracle.kept_counts_per_row(g, "temporal", 0, 31, rows)
+    assert list(got_s) == [_row_closed_spatial(F, H, W, 1, int(t)) for t in rows]
+    assert list(got_t) == [_row_closed_temporal(F, H, W, 31, int(t)) for t in rows]
+
+
+def test_mask_hand_examples():
+    ex = _golden("tiny_hand_examples.json")
+    g = Geometry(**ex["geometry"])
+    for e in ex["spatial_w1"]:
+        got = oracle.keep_matrix(g, "spatial", 1, 0, np.array([e["q"]]), np.array([e["k"]]))[0, 0]
+        assert bool(got) == e["keep"], e
+    for e in ex["temporal_r1"]:
+        got = oracle.keep_matrix(g, "temporal", 0, 1, np.array([e["q"]]), np.array([e["k"]]))[0, 0]
+        assert bool(got) == e["keep"], e
+
+
+def test_permutation_hand_examples_and_properties():
+    ex = _golden("tiny_hand_examples.json")
+    g = Geometry(**ex["geometry"])
+    perm = oracle.temporal_major_perm(g)
+    for pos, tok in ex["temporal_major_positions"]["pairs"]:
+        assert perm[pos] == tok
+    for g in (Geometry(4, 8, 8), Geometry(5, 24, 40), Geometry(2, 3, 5), Geometry(1, 4, 4)):
+        perm = oracle.temporal_major_perm(g)
+        P = g.patches
+        assert sorted(perm.tolist()) == list(range(g.n))          # bijection
+        assert (perm[:P] == np.arange(P)).all()                   # anchor block stays in front
+        f, y, x = oracle.frame_major_coords(g)
+        if g.frames > 1:
+            runs = perm[P:].reshape(P, g.frames - 1)              # one run per patch
+            assert (f[runs] == np.arange(1, g.frames)[None, :]).all()
+            assert ((runs % P) == np.arange(P)[:, None]).all()
+        x_tm = np.random.default_rng(0).standard_normal((g.n, 3))[perm]
+        back = oracle.unpermute_rows(x_tm, g)
+        assert (back[perm] == x_tm).all()
+
+
+def _inputs(seed, n, d, heads=1):
+    q = synth.random_bf16((heads, n, d), seed)
+    k = synth.random_bf16((heads, n, d), seed + 1)
+    v = synth.random_bf16((heads, n, d), seed + 2)
+    return q, k, v
+
+
+@pytest.mark.parametrize("kind,w,r", [("spatial", 1, 0), ("temporal", 0, 1), ("dense", 0, 0)])
+def test_attention_matches_torch_sdpa(kind, w, r):
+    """Same mask, torch's fp64 scaled_dot_product_attention as the reference."""
+    g = Geometry(4, 8, 8)
+    q, k, v = _inputs(10, g.n, 64)
+    scale = 0.125
+    o, lse = oracle.attend_head(q[0], k[0], v[0], scale, g, kind, w, r, block=100)
+    keep = oracle.keep_matrix(g, kind, w, r, np.arange(g.n), np.arange(g.n))
+    tq, tk, tv = (torch.from_numpy(oracle.bf16_to_f64(t[0])) for t in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq[None], tk[None], tv[None], attn_mask=torch.from_numpy(keep)[None], scale=scale)[0]
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    lref = torch.logsumexp(torch.where(torch.from_numpy(keep), (tq @ tk.T) * scale,
+                                       torch.tensor(-math.inf, dtype=torch.float64)), dim=1)
+    np.testing.assert_allclose(lse, lref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_pure_python_bruteforce():
+    """Per-row sums written with Python loops and math.exp (no numpy algebra)."""
+    g = Geometry(4, 8, 8)
+    d = 16
+    q, k, v = _inputs(20, g.n, d)
+    scale = float(np.float32(0.3))      # the oracle uses the fp32 scale both sides receive
+    rows = [0, 37, 64, 130, 255]
+    o, _ = oracle.attend_head(q[0], k[0], v[0], scale, g, "temporal", 0, 1, rows=np.array(rows))
+    Q, K, V = (oracle.bf16_to_f64(t[0]).tolist() for t in (q, k, v))
+    P, W = 64, 8
+    for n, i in enumerate(rows):
+        fi, yi, xi = i // P, (i % P) // W, (i % P) % W
+        kept = [j for j in range(g.n)
+                if j // P == 0 or max(abs(yi - (j % P) // W), abs(xi - (j % P) % W)) <= 1]
+        s = {j: scale * sum(Q[i][c] * K[j][c] for c in range(d)) for j in kept}
+        m = max(s.values())
+        z = sum(math.exp(s[j] - m) for j in kept)
+        for c in range(d):
+            ref = sum(math.exp(s[j] - m) * V[j][c] for j in kept) / z
+            assert abs(o[n][c] - ref) < 1e-12
+
+
+def test_q_zero_and_constant_v_closed_forms():
+    g = Geometry(4, 8, 8)
+    _, k, v = _inputs(30, g.n, 64)
+    q = np.zeros_like(k)
+    o, lse = oracle.attend_head(q[0], k[0], v[0], 0.125, g, "spatial", 1, 0)
+    vv = oracle.bf16_to_f64(v[0])
+    keep = oracle.keep_matrix(g, "spatial", 1, 0, np.arange(g.n), np.arange(g.n))
+    mean = (keep.astype(np.float64) @ vv) / keep.sum(1, keepdims=True)   # uniform weights
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.log(keep.sum(1)), rtol=0, atol=1e-12)
+    q2, k2, _ = _inputs(40, g.n, 64)
+    vc = np.full_like(k2, synth.f32_to_bf16_bits(np.float32([0.75]))[0])
+    o2, _ = oracle.attend_head(q2[0], k2[0], vc[0], 0.125, g, "temporal", 0, 1)
+    np.testing.assert_allclose(o2, 0.75, rtol=0, atol=1e-14)
+
+
+def test_output_inside_kept_value_range():
+    g = Geometry(5, 6, 7)
+    q, k, v = _inputs(50, g.n, 32)
+    o, _ = oracle.attend_head(q[0], k[0], v[0], 0.4, g, "temporal", 0, 2)
+    vv = oracle.bf16_to_f64(v[0])
+    keep = oracle.keep_matrix(g, "temporal", 0, 2, np.arange(g.n), np.arange(g.n))
+    for i in range(0, g.n, 17):
+        kv = vv[keep[i]]
+        assert (o[i] >= kv.min(0) - 1e-12).all() and (o[i] <= kv.max(0) + 1e-12).all()
+
+
+@pytest.mark.parametrize("F,H,W,r", [(4, 8, 8, 1), (5, 6, 10, 2)])
+def test_permute_attend_unpermute_equals_direct(F, H, W, r):
+    """Attention in the temporal-major order, mapped back, equals direct attention."""
+    g = Geometry(F, H, W)
+    q, k, v = _inputs(60, g.n, 32)
+    sc = float(np.float32(0.2))
+    direct, dl = oracle.attend_head(q[0], k[0], v[0], sc, g, "temporal", 0, r)
+    perm = oracle.temporal_major_perm(g)
+    Q, K, V = (oracle.bf16_to_f64(t[0])[perm] for t in (q, k, v))
+    keep_tm = oracle.keep_matrix(g, "temporal", 0, r, perm, perm)
+    o_tm, l_tm = oracle.attend_rows(Q, K, V, sc, keep_tm)
+    np.testing.assert_allclose(oracle.unpermute_rows(o_tm, g), direct, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.unpermute_rows(l_tm[:, None], g)[:, 0], dl, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Tile classes: an independent geometric derivation.
+#
+# A block's rows and its non-frame-0 columns each cover a set of patches that
+# is the union of at most two contiguous patch-index ranges, each of which is a
+# union of at most three grid rectangles.  Between two rectangles the smallest
+# Chebyshev distance is max(gap_y, gap_x) and the largest is
+# max(span_y, span_x), so a temporal block is non-empty iff some column is in
+# frame 0 or the smallest distance is <= r, and full iff every non-frame-0
+# column is within r of every row patch.  Spatial blocks use frame intervals the
+# same way.  Frame-0 columns are exactly positions < P in both orders.
+# ---------------------------------------------------------------------------
+
+def _rects(lo, hi, W):
+    ylo, yhi = lo // W, hi // W
+    if ylo == yhi:
+        return [(ylo, ylo, lo % W, hi % W)]
+    out = [(ylo, ylo, lo % W, W - 1), (yhi, yhi, 0, hi % W)]
+    if yhi > ylo + 1:
+        out.append((ylo + 1, yhi - 1, 0, W - 1))
+    return out
+
+
+def _patch_ranges(g, order, a, b):
+    """Contiguous patch-index ranges covered by positions [a, b)."""
+    P, F = g.patches, g.frames
+    if order == "fm":
+        if b - a >= P:
+            return [(0, P - 1)]
+        pa, pb = a % P, (b - 1) % P
+        return [(pa, pb)] if a // P == (b - 1) // P else [(pa, P - 1), (0, pb)]
+    out = []
+    if a < P:
+        out.append((a, min(b, P) - 1))
+    if b > P:
+        s = max(a, P)
+        out.append(((s - P) // (F - 1), (b - 1 - P) // (F - 1)))
+    return out
+
+
+def _frames(g, order, a, b):
+    assert order == "fm"
+    return a // g.patches, (b - 1) // g.patches
+
+
+def _geometric_class(g, kind, w, r, order, r0, r1, c0, c1):
+    P = g.patches
+    anchor = c0 < P
+    n0 = max(c0, P)
+    if n0 >= c1:
+        return 2                      # every column is in frame 0
+    if kind == "dense":
+        return 2
+    if kind == "spatial":
+        a, b = _frames(g, order, r0, r1)
+        c, d = _frames(g, order, n0, c1)
+        near_any = max(0, a - d, c - b) <= w
+        near_all = max(b - c, d - a) <= w
+    else:
+        R = [x for lo, hi in _patch_ranges(g, order, r0, r1) for x in _rects(lo, hi, g.width)]
+        C = [x for lo, hi in _patch_ranges(g, order, n0, c1) for x in _rects(lo, hi, g.width)]
+        dmin = min(max(max(0, A[0] - B[1], B[0] - A[1]), max(0, A[2] - B[3], B[2] - A[3]))
+                   for A in R for B in C)
+        dmax = max(max(A[1] - B[0], B[1] - A[0], A[3] - B[2], B[3] - A[2]) for A in R for B in C)
+        near_any, near_all = dmin <= r, dmax <= r
+    if near_all:
+        return 2
+    return 1 if (near_any or anchor) else 0
+
+
+def _geometric_map(g, kind, w, r, order, bq, bk, qtiles=None):
+    n = g.n
+    n_qt, n_kt = -(-n // bq), -(-n // bk)
+    qtiles = range(n_qt) if qtiles is None else qtiles
+    cls = np.zeros((len(qtiles), n_kt), dtype=np.uint8)
+    for i, qt in enumerate(qtiles):
+        for kt in range(n_kt):
+            cls[i, kt] = _geometric_class(g, kind, w, r, order, qt * bq, min(n, qt * bq + bq),
+                                          kt * bk, min(n, kt * bk + bk))
+    return cls
+
+
+CASES = [
+    (Geometry(4, 8, 8), "spatial", 1, 0, "fm", 32, 32),
+    (Geometry(4, 8, 8), "temporal", 0, 1, "fm", 32, 32),
+    (Geometry(4, 8, 8), "temporal", 0, 1, "tm", 32, 32),
+    (Geometry(4, 8, 8), "temporal", 0, 2, "tm", 64, 32),
+    (Geometry(4, 8, 8), "dense", 0, 0, "fm", 32, 64),
+    (Geometry(3, 5, 7), "temporal", 0, 1, "tm", 32, 32),     # ragged: N = 105
+    (Geometry(3, 5, 7), "spatial", 0, 0, "fm", 64, 32),
+] + [(Geometry(5, 24, 40), kind, w, r, order, bq, bk)
+     for (kind, w, r, order) in [("spatial", 1, 0, "fm"), ("temporal", 0, 2, "fm"), ("temporal", 0, 2, "tm")]
+     for bq in (64, 128) for bk in (64, 128)]
+
+
+@pytest.mark.parametrize("g,kind,w,r,order,bq,bk", CASES)
+def test_tile_classes_match_geometry(g, kind, w, r, order, bq, bk):
+    cls, row_ptr, col, col_cls = oracle.tile_map(g, kind, w, r, order, bq, bk)
+    assert (cls == _geometric_map(g, kind, w, r, order, bq, bk)).all()
+    # CSR is the ascending list of non-empty blocks per row
+    for qt in range(cls.shape[0]):
+        nz = np.nonzero(cls[qt])[0]
+        assert (col[row_ptr[qt]:row_ptr[qt + 1]] == nz).all()
+        assert (col_cls[row_ptr[qt]:row_ptr[qt + 1]] == cls[qt, nz]).all()
+    # block counts sum to the closed-form total
+    counts, _ = oracle.tile_counts(g, kind, w, r, order, bq, bk)
+    closed = {"spatial": lambda: _closed_spatial(g.frames, g.height, g.width, w),
+              "temporal": lambda: _closed_temporal(g.frames, g.height, g.width, r),
+              "dense": lambda: g.n ** 2}[kind]()
+    assert counts.sum() == closed
+
+
+def test_spatial_frame_aligned_tiles_are_never_boundary():
+    """With tiles that divide the frame, a block pairs one query frame with one
+    key frame, so it is all-kept or all-dropped: 12 of the 16 frame pairs are
+    kept at 4 frames with w=1 (closed form), i.e. 48 full and 16 empty 32x32 blocks."""
+    g = Geometry(4, 8, 8)
+    cls, *_ = oracle.tile_map(g, "spatial", 1, 0, "fm", 32, 32)
+    assert (cls == 1).sum() == 0
+    assert (cls == 2).sum() == 48 and (cls == 0).sum() == 16
+
+
+@pytest.mark.parametrize("kind,w,r,order", [("spatial", 1, 0, "fm"), ("temporal", 0, 31, "tm"),
+                                            ("temporal", 0, 31, "fm")])
+def test_headline_tile_rows_match_geometry(kind, w, r, order):
+    g = Geometry(21, 45, 80)
+    qtiles = [0, 14, 15, 150, 295]
+    cls, *_ = oracle.tile_map(g, kind, w, r, order, 256, 64, qtiles=qtiles)
+    assert (cls == _geometric_map(g, kind, w, r, order, 256, 64, qtiles=qtiles)).all()
