@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse spatio-temporal attention hot path on one MI355X.
+
+One step = one pass of the hot path over the workload's synthetic inputs,
+already resident in HBM: permute the temporal heads' Q/K/V to temporal-major
+order -> block-sparse attention forward over all heads -> unpermute the
+temporal heads' output.  Tile maps are built once per (geometry, mask, tile)
+and reused across steps (they do not depend on the activations); the
+classifier is timed separately, as are a dense-attention run of the same
+kernel (every tile full, no masking) and the naive traversal that masks every
+visited tile.
+
+Prints one JSON line.  `value` is effective TFLOP/s of the whole step
+(4 * head_dim * kept pairs, summed over heads, divided by ms_per_step);
+`roofline` is for the dominant kernel (the attention forward), timed with
+HIP events on the stream it is launched on.
+
+    python bench.py [--steps K] [--warmup W] [--workload headline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse attn fwd ms + effective TFLOP/s (% bf16 MFMA peak), 75.6K tok×10h×d128"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--block-q", type=int, default=256)
+    ap.add_argument("--block-k", type=int, default=64)
+    ap.add_argument("--temporal-order", choices=["tm", "fm"], default="tm")
+    ap.add_argument("--dense-steps", type=int, default=5)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the kernel on one MI355X and has no "
+              f"multi-GPU path (--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_spatio_svattn_amd as sv
+    from block_sparse_spatio_svattn_amd import metrics
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    import svattn_synth as synth
+
+    wl = synth.WORKLOADS[args.workload]
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    kinds = {synth.SPATIAL: sv.SPATIAL, synth.TEMPORAL: sv.TEMPORAL, synth.DENSE: sv.DENSE}
+    masks = []
+    for h in wl.heads:
+        tm = h.kind == synth.TEMPORAL and args.temporal_order == "tm"
+        masks.append(sv.Mask(kinds[h.kind], sv.TEMPORAL_MAJOR if tm else sv.FRAME_MAJOR, h.window, h.radius))
+    H, N, D = wl.n_heads, wl.n_tokens, wl.head_dim
+
+    log(f"workload {wl.name}: N={N} heads={H} d={D} tiles {args.block_q}x{args.block_k}")
+    t0 = time.time()
+    inp = synth.make_inputs(wl)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({3 * q.numel() * 2 / 1e9:.2f} GB, {time.time() - t0:.1f} s)")
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # ---- tile classifier (one-off per geometry/mask/tile), timed separately ----
+    layer = SparseVideoAttention(g, masks, D, args.block_q, args.block_k)
+    distinct = {}
+    for m, mp in zip(layer.masks, layer.maps):
+        distinct[(m.kind, m.order, m.window, m.radius)] = (m, mp)
+    torch.cuda.synchronize()
+    cls_ms = []
+    for _ in range(3):
+        a, b = ev(), ev()
+        a.record(stream)
+        for m, mp in distinct.values():
+            mp.rebuild(m)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cls_ms.append(a.elapsed_time(b))
+    nnz = {str(key): mp.nnz() for key, (m, mp) in distinct.items()}
+    log(f"classifier {min(cls_ms):.3f} ms for {len(distinct)} maps; nnz {nnz}")
+
+    # ---- warmup ----
+    for _ in range(args.warmup):
+        layer(q, k, v, scales, out=out)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # ---- timed steps ----
+    K = args.steps
+    marks = [[ev() for _ in range(4)] for _ in range(K)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        marks[i][0].record(stream)
+        layer.permute_inputs(q, k, v)
+        marks[i][1].record(stream)
+        layer.attend(q, k, v, out, scales)
+        marks[i][2].record(stream)
+        layer.unpermute_output(out)
+        marks[i][3].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    perm_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    fwd_all = np.array([m[1].elapsed_time(m[2]) for m in marks])
+    fwd_ms = float(np.mean(fwd_all))
+    unperm_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    log(f"step {ms_step:.3f} ms: permute {perm_ms:.3f} + forward {fwd_ms:.3f} (min {fwd_all.min():.3f}) "
+        f"+ unpermute {unperm_ms:.3f}")
+
+    flops = metrics.effective_flops(g, masks, D)
+    kept = sum(metrics.kept_pairs(g, m) for m in masks)
+    kept_frac = kept / (H * N * N)
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    peak = metrics.BF16_PEAK_TFLOPS
+
+    extra = {}
+    # ---- dense comparator: the same kernel, every tile full ----
+    if not args.no_dense:
+        dmask = [sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0)] * H
+        dense = SparseVideoAttention(g, dmask, D, args.block_q, args.block_k)
+        dense.attend(q, k, v, out, scales)
+        torch.cuda.synchronize()
+        dm = []
+        for _ in range(args.dense_steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            dense.attend(q, k, v, out, scales)
+            b.record(stream)
+            dm.append((a, b))
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in dm]))
+        dense_flops = metrics.effective_flops(g, dmask, D)
+        extra["dense"] = {"ms": round(dense_ms, 4),
+                          "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+                          "pct_peak": round(100 * dense_flops / (dense_ms * 1e-3) / 1e12 / peak, 2),
+                          "sparse_speedup": round(dense_ms / fwd_ms, 3)}
+        log(f"dense comparator {dense_ms:.3f} ms -> sparse speedup {dense_ms / fwd_ms:.2f}x")
+        del dense
+    # ---- naive traversal: every visited tile masked ----
+    if not args.no_naive:
+        naive = SparseVideoAttention(g, masks, D, args.block_q, args.block_k, map_flags=sv.MAP_ALL_BOUNDARY)
+        naive.permute_inputs(q, k, v)
+        naive.attend(q, k, v, out, scales)
+        torch.cuda.synchronize()
+        nm = []
+        for _ in range(max(3, args.dense_steps)):
+            a, b = ev(), ev()
+            a.record(stream)
+            naive.attend(q, k, v, out, scales)
+            b.record(stream)
+            nm.append((a, b))
+        torch.cuda.synchronize()
+        naive_ms = float(np.mean([a.elapsed_time(b) for a, b in nm]))
+        extra["naive_all_boundary"] = {"ms": round(naive_ms, 4), "slowdown_vs_full_boundary": round(naive_ms / fwd_ms, 3)}
+        log(f"naive (every tile masked) {naive_ms:.3f} ms")
+        del naive
+
+    # ---- CPU oracle baseline (bounded sample) ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        log(f"cpu oracle baseline {cpu}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": N, "frames": wl.frames, "grid": [wl.height, wl.width],
+                   "heads": H, "head_dim": D, "block_q": args.block_q, "block_k": args.block_k,
+                   "spatial_heads": sum(1 for h in wl.heads if h.kind == synth.SPATIAL),
+                   "temporal_heads": sum(1 for h in wl.heads if h.kind == synth.TEMPORAL),
+                   "temporal_order": args.temporal_order, "kept_fraction": round(kept_frac, 6),
+                   "parallelism": "single-gpu"},
+        "fwd_kernel": {"ms": round(fwd_ms, 4), "ms_min": round(float(fwd_all.min()), 4),
+                       "tflops": round(fwd_tflops, 2), "pct_bf16_peak": round(100 * fwd_tflops / peak, 2)},
+        "permute_ms": round(perm_ms, 4),
+        "unpermute_ms": round(unperm_ms, 4),
+        "classifier_ms": round(min(cls_ms), 4),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fwd_tflops / peak, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, inp, seconds):
+    """The fp64 oracle, as it stands, on a bounded seeded sample of query rows."""
+    import numpy as np
+    import oracle
+    import svattn_synth as synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+
+    def run(rows_per_head):
+        rows = synth.sample_rows(wl, rows_per_head)
+        fl = 0.0
+        t = time.perf_counter()
+        for h, head in enumerate(wl.heads):
+            oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind, head.window,
+                               head.radius, rows=rows[h])
+        dt = time.perf_counter() - t
+        for h, head in enumerate(wl.heads):
+            fl += 4 * wl.head_dim * float(oracle.kept_counts_per_row(g, head.kind, head.window, head.radius,
+                                                                     rows[h]).sum())
+        return dt, fl
+
+    dt, fl = run(8)
+    r = int(max(8, min(4096, 8 * seconds / max(dt, 1e-3))))
+    dt, fl = run(r)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{r} seeded query rows per head x {wl.n_heads} heads of {wl.n_tokens}, fp64 numpy, "
+                      f"{dt:.1f} s wall", "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,420 @@
+// C ABI of libsvattn.so: argument validation, per-head launch tables and
+// dispatch.  Every check runs before the first HIP call, so invalid calls
+// return a status without touching the GPU.  No allocation, no host sync.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "internal.hpp"
+
+namespace svattn {
+hipError_t launch_forward_d64(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
+hipError_t launch_forward_d128(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
+}  // namespace svattn
+
+using namespace svattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SVATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int64_t kMaxTokens = 1 << 24;
+
+int check_geom(const svattn_geom* g, int64_t* n_out) {
+  if (!g) return fail(SVATTN_ERR_INVALID_ARG, "geom is NULL");
+  if (g->frames < 1 || g->height < 1 || g->width < 1)
+    return fail(SVATTN_ERR_INVALID_ARG, "geometry %d x %d x %d: every extent must be >= 1", g->frames,
+                g->height, g->width);
+  const int64_t n = (int64_t)g->frames * g->height * g->width;
+  if (n > kMaxTokens) return fail(SVATTN_ERR_UNSUPPORTED, "N = %lld tokens exceeds %lld", (long long)n,
+                                  (long long)kMaxTokens);
+  *n_out = n;
+  return SVATTN_OK;
+}
+
+int check_mask(const svattn_mask* m) {
+  if (!m) return fail(SVATTN_ERR_INVALID_ARG, "mask is NULL");
+  if (m->kind < SVATTN_SPATIAL || m->kind > SVATTN_DENSE)
+    return fail(SVATTN_ERR_INVALID_ARG, "mask kind %d is not SPATIAL/TEMPORAL/DENSE", m->kind);
+  if (m->order != SVATTN_FRAME_MAJOR && m->order != SVATTN_TEMPORAL_MAJOR)
+    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not FRAME_MAJOR/TEMPORAL_MAJOR", m->order);
+  if (m->window < 0 || m->radius < 0)
+    return fail(SVATTN_ERR_INVALID_ARG, "window %d / radius %d must be >= 0", m->window, m->radius);
+  if (m->kind == SVATTN_SPATIAL && m->order != SVATTN_FRAME_MAJOR)
+    return fail(SVATTN_ERR_UNSUPPORTED, "spatial heads run in frame-major order only");
+  return SVATTN_OK;
+}
+
+bool map_bq_ok(int b) { return b == 32 || b == 64 || b == 128 || b == 256; }
+bool map_bk_ok(int b) { return b == 32 || b == 64 || b == 128; }
+bool fwd_bk_ok(int b) { return b == 32 || b == 64; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Kept query-key pairs of a head (closed form), used only to order heads
+// longest-first.
+double head_cost(const svattn_geom& g, const svattn_mask& m) {
+  const double F = g.frames, P = (double)g.height * g.width, N = F * P;
+  if (m.kind == SVATTN_DENSE) return N * N;
+  if (m.kind == SVATTN_SPATIAL) {
+    const int w = m.window;
+    if (w >= g.frames - 1) return N * N;
+    return P * P * (F * (2 * w + 1) - (double)w * (w + 1) + std::max(0, g.frames - 1 - w));
+  }
+  auto sw = [](int L, int r) { return r >= L - 1 ? (double)L * L : (double)L * (2 * r + 1) - (double)r * (r + 1); };
+  double c = F * (F - 1) * sw(g.height, m.radius) * sw(g.width, m.radius) + F * P * P;
+  if (m.order == SVATTN_FRAME_MAJOR) c *= 1.5;  // frame-major temporal heads visit more tiles
+  return c;
+}
+
+int check_map_buffers(const svattn_tile_map* map, const char* who) {
+  if (!map->cls || !map->row_ptr || !map->col || !map->col_cls)
+    return fail(SVATTN_ERR_INVALID_ARG, "%s: tile map buffer is NULL", who);
+  return SVATTN_OK;
+}
+
+hipError_t dispatch_forward(const FwdArgs& a, int head_dim, int bq, int bk, hipStream_t st) {
+  return head_dim == 128 ? launch_forward_d128(a, bq, bk, st) : launch_forward_d64(a, bq, bk, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int svattn_version(void) { return SVATTN_VERSION; }
+
+const char* svattn_status_string(int s) {
+  switch (s) {
+    case SVATTN_OK: return "SVATTN_OK";
+    case SVATTN_ERR_INVALID_ARG: return "SVATTN_ERR_INVALID_ARG";
+    case SVATTN_ERR_UNSUPPORTED: return "SVATTN_ERR_UNSUPPORTED";
+    case SVATTN_ERR_HIP: return "SVATTN_ERR_HIP";
+    default: return "SVATTN_ERR_UNKNOWN";
+  }
+}
+
+const char* svattn_last_error(void) { return g_err; }
+
+int svattn_tile_map_dims(const svattn_geom* geom, int32_t block_q, int32_t block_k, int32_t* n_qt,
+                         int32_t* n_kt) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if (!n_qt || !n_kt) return fail(SVATTN_ERR_INVALID_ARG, "n_qt / n_kt output is NULL");
+  if (!map_bq_ok(block_q) || !map_bk_ok(block_k))
+    return fail(SVATTN_ERR_UNSUPPORTED, "tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64,128}",
+                block_q, block_k);
+  *n_qt = (int32_t)cdiv(n, block_q);
+  *n_kt = (int32_t)cdiv(n, block_k);
+  return SVATTN_OK;
+}
+
+int svattn_build_tile_map_ex(const svattn_geom* geom, const svattn_mask* mask, svattn_tile_map* map,
+                             uint32_t flags, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if ((s = check_mask(mask))) return s;
+  if (!map) return fail(SVATTN_ERR_INVALID_ARG, "map is NULL");
+  if (flags & ~SVATTN_MAP_ALL_BOUNDARY) return fail(SVATTN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!map_bq_ok(map->block_q) || !map_bk_ok(map->block_k))
+    return fail(SVATTN_ERR_UNSUPPORTED, "tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64,128}",
+                map->block_q, map->block_k);
+  if (map->n_qt != cdiv(n, map->block_q) || map->n_kt != cdiv(n, map->block_k))
+    return fail(SVATTN_ERR_INVALID_ARG, "map dims %d x %d do not match ceil(N/block) = %lld x %lld", map->n_qt,
+                map->n_kt, (long long)cdiv(n, map->block_q), (long long)cdiv(n, map->block_k));
+  if ((int64_t)map->n_qt * map->n_kt >= (1ll << 31))
+    return fail(SVATTN_ERR_UNSUPPORTED, "tile map of %d x %d blocks is too large", map->n_qt, map->n_kt);
+  if ((s = check_map_buffers(map, "svattn_build_tile_map"))) return s;
+  if (!aligned(map->row_ptr, 4) || !aligned(map->col, 4))
+    return fail(SVATTN_ERR_INVALID_ARG, "row_ptr / col must be 4-byte aligned");
+  const Geo g = make_geo(*geom);
+  hipError_t e = launch_tile_map(g, *mask, *map, flags, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tile map launch");
+  return SVATTN_OK;
+}
+
+int svattn_build_tile_map(const svattn_geom* geom, const svattn_mask* mask, svattn_tile_map* map,
+                          void* stream) {
+  return svattn_build_tile_map_ex(geom, mask, map, 0u, stream);
+}
+
+int svattn_permutation_index(const svattn_geom* geom, int32_t* perm, int32_t* inv, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if (!perm) return fail(SVATTN_ERR_INVALID_ARG, "perm is NULL");
+  if (!aligned(perm, 4) || (inv && !aligned(inv, 4)))
+    return fail(SVATTN_ERR_INVALID_ARG, "perm / inv must be 4-byte aligned");
+  if (inv && overlap(perm, n * 4, inv, n * 4)) return fail(SVATTN_ERR_INVALID_ARG, "perm and inv overlap");
+  hipError_t e = launch_perm_index(make_geo(*geom), perm, inv, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "permutation index launch");
+  return SVATTN_OK;
+}
+
+static int permute_common(const svattn_geom* geom, int32_t heads, int32_t head_dim, const void* src, void* dst,
+                          bool to_tm, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if (heads < 1) return fail(SVATTN_ERR_INVALID_ARG, "heads = %d must be >= 1", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SVATTN_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);
+  if (!src || !dst) return fail(SVATTN_ERR_INVALID_ARG, "src / dst is NULL");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(SVATTN_ERR_INVALID_ARG, "src / dst must be 16-byte aligned");
+  const int64_t chunks = (int64_t)heads * n * (head_dim / 8);
+  if (chunks >= (1ll << 31)) return fail(SVATTN_ERR_UNSUPPORTED, "tensor too large (%lld rows)", (long long)(heads * n));
+  const size_t bytes = (size_t)heads * n * head_dim * 2;
+  if (overlap(src, bytes, dst, bytes)) return fail(SVATTN_ERR_INVALID_ARG, "src and dst overlap (no in-place)");
+  hipError_t e = launch_permute(make_geo(*geom), heads, head_dim, src, dst, to_tm, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return SVATTN_OK;
+}
+
+int svattn_permute_tokens(const svattn_geom* geom, int32_t heads, int32_t head_dim, const void* src, void* dst,
+                          void* stream) {
+  return permute_common(geom, heads, head_dim, src, dst, true, stream);
+}
+
+int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t head_dim, const void* src, void* dst,
+                     void* stream) {
+  return permute_common(geom, heads, head_dim, src, dst, false, stream);
+}
+
+static int check_common(int32_t heads, int32_t head_dim, const float* scales) {
+  if (heads < 1) return fail(SVATTN_ERR_INVALID_ARG, "heads = %d must be >= 1", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SVATTN_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);
+  if (!scales) return fail(SVATTN_ERR_INVALID_ARG, "scales is NULL");
+  for (int h = 0; h < heads; ++h)
+    if (!(scales[h] > 0.f) || !isfinite(scales[h]))
+      return fail(SVATTN_ERR_INVALID_ARG, "scales[%d] = %g must be finite and > 0", h, (double)scales[h]);
+  return SVATTN_OK;
+}
+
+// Per-head tensor pointers: q/k/v/o [N, head_dim] bf16 each, lse [N] fp32 or NULL.
+struct HeadPtrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+};
+
+static int check_ptrs(const std::vector<HeadPtrs>& p, int64_t n, int32_t head_dim) {
+  const size_t bytes = (size_t)n * head_dim * 2, lb = (size_t)n * 4;
+  for (size_t h = 0; h < p.size(); ++h) {
+    if (!p[h].q || !p[h].k || !p[h].v || !p[h].o)
+      return fail(SVATTN_ERR_INVALID_ARG, "head %zu: q / k / v / o is NULL", h);
+    if (!aligned(p[h].q, 16) || !aligned(p[h].k, 16) || !aligned(p[h].v, 16) || !aligned(p[h].o, 16))
+      return fail(SVATTN_ERR_INVALID_ARG, "head %zu: q / k / v / o must be 16-byte aligned", h);
+    if (p[h].lse && !aligned(p[h].lse, 4)) return fail(SVATTN_ERR_INVALID_ARG, "head %zu: lse must be 4-byte aligned", h);
+  }
+  // outputs must not overlap any input or each other
+  for (size_t h = 0; h < p.size(); ++h) {
+    for (size_t j = 0; j < p.size(); ++j) {
+      if (overlap(p[h].o, bytes, p[j].q, bytes) || overlap(p[h].o, bytes, p[j].k, bytes) ||
+          overlap(p[h].o, bytes, p[j].v, bytes))
+        return fail(SVATTN_ERR_INVALID_ARG, "o of head %zu overlaps q, k or v of head %zu", h, j);
+      if (j != h && overlap(p[h].o, bytes, p[j].o, bytes))
+        return fail(SVATTN_ERR_INVALID_ARG, "o of heads %zu and %zu overlap", h, j);
+      if (p[h].lse) {
+        if (overlap(p[h].lse, lb, p[j].q, bytes) || overlap(p[h].lse, lb, p[j].k, bytes) ||
+            overlap(p[h].lse, lb, p[j].v, bytes) || overlap(p[h].lse, lb, p[j].o, bytes))
+          return fail(SVATTN_ERR_INVALID_ARG, "lse of head %zu overlaps a tensor of head %zu", h, j);
+        if (j != h && p[j].lse && overlap(p[h].lse, lb, p[j].lse, lb))
+          return fail(SVATTN_ERR_INVALID_ARG, "lse of heads %zu and %zu overlap", h, j);
+      }
+    }
+  }
+  return SVATTN_OK;
+}
+
+static std::vector<HeadPtrs> contiguous_ptrs(int64_t n, int32_t heads, int32_t head_dim, const void* q,
+                                             const void* k, const void* v, void* o, float* lse) {
+  std::vector<HeadPtrs> p(heads);
+  const size_t hb = (size_t)n * head_dim * 2;
+  for (int h = 0; h < heads; ++h) {
+    p[h].q = q ? (const char*)q + h * hb : nullptr;
+    p[h].k = k ? (const char*)k + h * hb : nullptr;
+    p[h].v = v ? (const char*)v + h * hb : nullptr;
+    p[h].o = o ? (char*)o + h * hb : nullptr;
+    p[h].lse = lse ? lse + (size_t)h * n : nullptr;
+  }
+  return p;
+}
+
+static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int head_dim, int bq, int bk,
+                        hipStream_t st) {
+  for (size_t h0 = 0; h0 < descs.size(); h0 += kMaxHeadsPerLaunch) {
+    FwdArgs a = base;
+    const int nh = (int)std::min<size_t>(kMaxHeadsPerLaunch, descs.size() - h0);
+    for (int i = 0; i < nh; ++i) a.heads[i] = descs[h0 + i];
+    a.n_slots = nh;
+    a.n_items = nh * a.n_qt;
+    hipError_t e = dispatch_forward(a, head_dim, bq, bk, st);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
+  return SVATTN_OK;
+}
+
+static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32_t head_dim,
+                        const svattn_mask* masks, const svattn_tile_map* const* maps, const float* scales,
+                        const std::vector<HeadPtrs>& ptrs, void* stream) {
+  int s;
+  if (!masks || !maps) return fail(SVATTN_ERR_INVALID_ARG, "masks / maps is NULL");
+  int bq = 0, bk = 0;
+  for (int h = 0; h < heads; ++h) {
+    if ((s = check_mask(&masks[h]))) return fail(s, "head %d: %s", h, svattn_last_error());
+    const svattn_tile_map* m = maps[h];
+    if (!m) return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] is NULL", h);
+    if (h == 0) {
+      bq = m->block_q;
+      bk = m->block_k;
+    } else if (m->block_q != bq || m->block_k != bk) {
+      return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] tile %d x %d differs from maps[0] %d x %d", h, m->block_q,
+                  m->block_k, bq, bk);
+    }
+    if (!map_bq_ok(bq) || !fwd_bk_ok(bk))
+      return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64}",
+                  bq, bk);
+    if (m->n_qt != cdiv(n, bq) || m->n_kt != cdiv(n, bk))
+      return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] dims %d x %d do not match the geometry", h, m->n_qt, m->n_kt);
+    if (!m->row_ptr || !m->col || !m->col_cls) return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] buffer is NULL", h);
+  }
+  if ((s = check_ptrs(ptrs, n, head_dim))) return s;
+
+  std::vector<HeadDesc> descs(heads);
+  std::vector<double> cost(heads);
+  std::vector<int> order(heads);
+  for (int h = 0; h < heads; ++h) {
+    HeadDesc& d = descs[h];
+    memset(&d, 0, sizeof(d));
+    d.q = ptrs[h].q;
+    d.k = ptrs[h].k;
+    d.v = ptrs[h].v;
+    d.o = ptrs[h].o;
+    d.lse = ptrs[h].lse;
+    d.row_ptr = maps[h]->row_ptr;
+    d.col = maps[h]->col;
+    d.col_cls = maps[h]->col_cls;
+    d.scale = scales[h];
+    d.scale_log2 = scales[h] * kLog2eHost;
+    d.kind = masks[h].kind;
+    d.order = masks[h].order;
+    d.window = masks[h].window;
+    d.radius = masks[h].radius;
+    cost[h] = head_cost(*geom, masks[h]);
+    order[h] = h;
+  }
+  // Longest heads first so the tail of the grid is short work.
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost[x] > cost[y]; });
+  std::vector<HeadDesc> sorted(heads);
+  for (int i = 0; i < heads; ++i) sorted[i] = descs[order[i]];
+
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geo(*geom);
+  a.n_qt = (int32_t)cdiv(n, bq);
+  a.n_kt = (int32_t)cdiv(n, bk);
+  a.chunk = 32;
+  a.dense_bits = 0;
+  return run_launches(a, sorted, head_dim, bq, bk, (hipStream_t)stream);
+}
+
+int svattn_forward(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
+                   const svattn_tile_map* const* maps, const float* scales, const void* q, const void* k,
+                   const void* v, void* o, float* lse, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if ((s = check_common(heads, head_dim, scales))) return s;
+  if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
+  return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
+                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), stream);
+}
+
+int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
+                        const svattn_tile_map* const* maps, const float* scales, const void* const* q,
+                        const void* const* k, const void* const* v, void* const* o, float* const* lse,
+                        void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if ((s = check_common(heads, head_dim, scales))) return s;
+  if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o pointer array is NULL");
+  std::vector<HeadPtrs> p(heads);
+  for (int h = 0; h < heads; ++h) p[h] = HeadPtrs{q[h], k[h], v[h], o[h], lse ? lse[h] : nullptr};
+  return forward_impl(geom, n, heads, head_dim, masks, maps, scales, p, stream);
+}
+
+int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim, const uint32_t* mask_bits,
+                              int32_t per_head, const float* scales, const void* q, const void* k, const void* v,
+                              void* o, float* lse, int32_t block_q, int32_t block_k, void* stream) {
+  if (n_tokens < 1 || n_tokens > kMaxTokens)
+    return fail(SVATTN_ERR_INVALID_ARG, "n_tokens = %d must be in [1, %lld]", n_tokens, (long long)kMaxTokens);
+  const int64_t n = n_tokens;
+  int s = check_common(heads, head_dim, scales);
+  if (s) return s;
+  if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
+  if (!mask_bits) return fail(SVATTN_ERR_INVALID_ARG, "mask_bits is NULL");
+  if (!aligned(mask_bits, 4)) return fail(SVATTN_ERR_INVALID_ARG, "mask_bits must be 4-byte aligned");
+  if (!map_bq_ok(block_q) || !fwd_bk_ok(block_k))
+    return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64}",
+                block_q, block_k);
+  const std::vector<HeadPtrs> ptrs = contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse);
+  if ((s = check_ptrs(ptrs, n, head_dim))) return s;
+  const int64_t wpr = cdiv(n, 32);
+  const size_t mb = (size_t)(per_head ? heads : 1) * n * wpr * 4, hb = (size_t)heads * n * head_dim * 2;
+  if (overlap(mask_bits, mb, o, hb)) return fail(SVATTN_ERR_INVALID_ARG, "mask_bits overlaps o");
+  std::vector<HeadDesc> descs(heads);
+  for (int h = 0; h < heads; ++h) {
+    HeadDesc& d = descs[h];
+    memset(&d, 0, sizeof(d));
+    d.q = ptrs[h].q;
+    d.k = ptrs[h].k;
+    d.v = ptrs[h].v;
+    d.o = ptrs[h].o;
+    d.lse = ptrs[h].lse;
+    d.bits = mask_bits + (per_head ? (size_t)h * n * wpr : 0);
+    d.scale = scales[h];
+    d.scale_log2 = scales[h] * kLog2eHost;
+    d.kind = SVATTN_DENSE;
+  }
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  svattn_geom g1 = {1, 1, n_tokens};
+  a.g = make_geo(g1);
+  a.n_qt = (int32_t)cdiv(n, block_q);
+  a.n_kt = (int32_t)cdiv(n, block_k);
+  a.chunk = 32;
+  a.dense_bits = 1;
+  a.words_per_row = (int32_t)wpr;
+  return run_launches(a, descs, head_dim, block_q, block_k, (hipStream_t)stream);
+}
+
+}  // extern "C"

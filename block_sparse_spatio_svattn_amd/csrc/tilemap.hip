@@ -1,0 +1,212 @@
+// Tile classifier and CSR compaction.
+//
+// A (q-tile, k-tile) block is EMPTY when no pair in it is kept, FULL when every
+// in-range pair is kept, BOUNDARY otherwise; the attention kernel skips EMPTY
+// blocks, runs FULL blocks without a mask and evaluates the coordinate mask
+// only on BOUNDARY blocks ("Accelerating Spatio-Temporal Attention for Video
+// Diffusion on TPUs", aihirek.info, section "A TPU-kernel kialakítása
+// döntőnek bizonyult", paragraphs 2-3).
+//
+// Classes are exact and computed from coordinates, one thread per block, with
+// no per-pair work: the rows of a block cover a set of patches that is the
+// union of at most two contiguous patch-index ranges (a frame-major range can
+// wrap once around a frame boundary; an anchor-first temporal-major range can
+// straddle the frame-0 prefix), and each range is at most three grid
+// rectangles.  Between two rectangles the smallest Chebyshev distance is
+// max(gap_y, gap_x) and the largest is max(span_y, span_x).  Key positions
+// below P (frame 0, the anchor) are kept for every query in both orders.
+
+#include "internal.hpp"
+
+namespace svattn {
+namespace {
+
+struct Rect {
+  int y0, y1, x0, x1;
+};
+
+// Contiguous patch-index ranges [lo, hi] covered by positions [a, b), b > a.
+__device__ int patch_ranges(const Geo& g, int order, int a, int b, int2 out[2]) {
+  if (order == SVATTN_FRAME_MAJOR) {
+    if (b - a >= g.P) {
+      out[0] = make_int2(0, g.P - 1);
+      return 1;
+    }
+    uint32_t fa = g.divP.div((uint32_t)a), fb = g.divP.div((uint32_t)(b - 1));
+    int pa = a - (int)fa * g.P, pb = (b - 1) - (int)fb * g.P;
+    if (fa == fb) {
+      out[0] = make_int2(pa, pb);
+      return 1;
+    }
+    out[0] = make_int2(pa, g.P - 1);
+    out[1] = make_int2(0, pb);
+    return 2;
+  }
+  int n = 0;
+  if (a < g.P) out[n++] = make_int2(a, min(b, g.P) - 1);
+  if (b > g.P) {
+    int s = max(a, g.P);
+    out[n++] = make_int2((int)g.divF1.div((uint32_t)(s - g.P)), (int)g.divF1.div((uint32_t)(b - 1 - g.P)));
+  }
+  return n;
+}
+
+__device__ int rects_of(const Geo& g, int2 r, Rect* out) {
+  int ylo = (int)g.divW.div((uint32_t)r.x), yhi = (int)g.divW.div((uint32_t)r.y);
+  int xlo = r.x - ylo * g.W, xhi = r.y - yhi * g.W;
+  if (ylo == yhi) {
+    out[0] = Rect{ylo, ylo, xlo, xhi};
+    return 1;
+  }
+  out[0] = Rect{ylo, ylo, xlo, g.W - 1};
+  out[1] = Rect{yhi, yhi, 0, xhi};
+  if (yhi > ylo + 1) {
+    out[2] = Rect{ylo + 1, yhi - 1, 0, g.W - 1};
+    return 3;
+  }
+  return 2;
+}
+
+__device__ int rect_set(const Geo& g, int order, int a, int b, Rect out[6]) {
+  int2 rg[2];
+  int nr = patch_ranges(g, order, a, b, rg);
+  int n = 0;
+  for (int i = 0; i < nr; ++i) n += rects_of(g, rg[i], out + n);
+  return n;
+}
+
+// Class of the block rows [r0, r1) x columns [c0, c1) (both clipped to N).
+__device__ uint8_t classify(const Geo& g, const svattn_mask& m, int r0, int r1, int c0, int c1) {
+  const bool anchor = c0 < g.P;  // some key of the block is in frame 0
+  const int n0 = max(c0, g.P);   // first key outside frame 0
+  if (n0 >= c1 || m.kind == SVATTN_DENSE) return SVATTN_TILE_FULL;
+  bool near_any, near_all;
+  if (m.kind == SVATTN_SPATIAL) {  // frame-major only: frames of a range are an interval
+    int a = (int)g.divP.div((uint32_t)r0), b = (int)g.divP.div((uint32_t)(r1 - 1));
+    int c = (int)g.divP.div((uint32_t)n0), d = (int)g.divP.div((uint32_t)(c1 - 1));
+    near_any = max(0, max(a - d, c - b)) <= m.window;
+    near_all = max(b - c, d - a) <= m.window;
+  } else {
+    Rect R[6], C[6];
+    int nr = rect_set(g, m.order, r0, r1, R);
+    int nc = rect_set(g, m.order, n0, c1, C);
+    int dmin = 1 << 30, dmax = 0;
+    for (int i = 0; i < nr; ++i) {
+      for (int j = 0; j < nc; ++j) {
+        int gy = max(0, max(R[i].y0 - C[j].y1, C[j].y0 - R[i].y1));
+        int gx = max(0, max(R[i].x0 - C[j].x1, C[j].x0 - R[i].x1));
+        dmin = min(dmin, max(gy, gx));
+        int sy = max(R[i].y1 - C[j].y0, C[j].y1 - R[i].y0);
+        int sx = max(R[i].x1 - C[j].x0, C[j].x1 - R[i].x0);
+        dmax = max(dmax, max(sy, sx));
+      }
+    }
+    near_any = dmin <= m.radius;
+    near_all = dmax <= m.radius;
+  }
+  if (near_all) return SVATTN_TILE_FULL;
+  return (near_any || anchor) ? SVATTN_TILE_BOUNDARY : SVATTN_TILE_EMPTY;
+}
+
+constexpr int kThreads = 256;
+
+__device__ int block_sum(int v, int* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Pass 1: classes of one q-tile row; row_ptr[qt+1] = number of non-empty blocks.
+__global__ __launch_bounds__(kThreads) void classify_kernel(Geo g, svattn_mask m, svattn_tile_map map,
+                                                            uint32_t flags) {
+  __shared__ int red[kThreads / 64];
+  const int qt = blockIdx.x;
+  const int r0 = qt * map.block_q, r1 = min(g.N, r0 + map.block_q);
+  int count = 0;
+  for (int kt = threadIdx.x; kt < map.n_kt; kt += kThreads) {
+    const int c0 = kt * map.block_k, c1 = min(g.N, c0 + map.block_k);
+    uint8_t c = classify(g, m, r0, r1, c0, c1);
+    if ((flags & SVATTN_MAP_ALL_BOUNDARY) && c != SVATTN_TILE_EMPTY) c = SVATTN_TILE_BOUNDARY;
+    map.cls[(size_t)qt * map.n_kt + kt] = c;
+    count += (c != SVATTN_TILE_EMPTY);
+  }
+  count = block_sum(count, red);
+  if (threadIdx.x == 0) {
+    map.row_ptr[qt + 1] = count;
+    if (qt == 0) map.row_ptr[0] = 0;
+  }
+}
+
+// Pass 2: in-place inclusive scan of row_ptr[1..n] by one workgroup.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* row_ptr, int n) {
+  __shared__ int part[kScanThreads];
+  const int t = threadIdx.x;
+  const int seg = (n + kScanThreads - 1) / kScanThreads;
+  const int lo = 1 + t * seg, hi = min(n + 1, lo + seg);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += row_ptr[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {  // Hillis-Steele inclusive scan
+    int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = t > 0 ? part[t - 1] : 0;
+  for (int i = lo; i < hi; ++i) {
+    run += row_ptr[i];
+    row_ptr[i] = run;
+  }
+}
+
+// Pass 3: ascending list of non-empty k-tiles of each q-tile row.
+__global__ __launch_bounds__(kThreads) void compact_kernel(svattn_tile_map map) {
+  __shared__ int wave_cnt[kThreads / 64];
+  const int qt = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int base = map.row_ptr[qt];
+  const uint8_t* row = map.cls + (size_t)qt * map.n_kt;
+  for (int k0 = 0; k0 < map.n_kt; k0 += kThreads) {
+    const int kt = k0 + threadIdx.x;
+    const uint8_t c = kt < map.n_kt ? row[kt] : SVATTN_TILE_EMPTY;
+    const bool nz = c != SVATTN_TILE_EMPTY;
+    const uint64_t bal = __ballot(nz);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base, total = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      if (w < wave) off += wave_cnt[w];
+      total += wave_cnt[w];
+    }
+    if (nz) {
+      map.col[off + before] = kt;
+      map.col_cls[off + before] = c;
+    }
+    base += total;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_map(const Geo& g, const svattn_mask& m, const svattn_tile_map& map, uint32_t flags,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(classify_kernel, dim3(map.n_qt), dim3(kThreads), 0, st, g, m, map, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, map.row_ptr, map.n_qt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3(map.n_qt), dim3(kThreads), 0, st, map);
+  return hipGetLastError();
+}
+
+}  // namespace svattn

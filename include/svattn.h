@@ -1,0 +1,205 @@
+/*
+ * svattn.h -- C ABI of the MI355X (gfx950) block-sparse spatio-temporal
+ * attention library (libsvattn.so).
+ *
+ * The method: Sparse-VideoGen-style self-attention for video diffusion, where
+ * every head is either spatial (keys in the query's own and nearby frames) or
+ * temporal (keys at nearby patch positions in every frame), and both kinds
+ * always keep every key of the first frame as an anchor ("Accelerating
+ * Spatio-Temporal Attention for Video Diffusion on TPUs", Google for
+ * Developers, as retold on aihirek.info, section "A Sparse VideoGen a figyelmi
+ * fejeket osztályozza", paragraphs 2-3).  The kernel work is tiled: tiles with
+ * no kept pair are skipped, fully kept tiles run without any mask, and only
+ * boundary tiles evaluate the coordinate mask (same page, section "A
+ * TPU-kernel kialakítása döntőnek bizonyult", paragraphs 2-3).  Temporal heads
+ * may be run in a temporal-major token order (ainews.tenesys.com, list "Co się
+ * zmieniło?", item 5).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Buffers must stay valid until the
+ *     work queued on `stream` has completed.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     GPU work is queued asynchronously on it; no entry point synchronises the
+ *     host.
+ *   - Tokens: a video latent of F frames x H x W patches, P = H*W patches per
+ *     frame, N = F*P tokens.  Frame-major token t = f*P + y*W + x.
+ *     Temporal-major position t' (anchor-first): t' < P holds frame 0, patch
+ *     t'; otherwise u = t'-P holds patch u / (F-1) of frame 1 + u % (F-1).
+ *   - Q, K, V, O: bf16, contiguous [heads, N, head_dim], 16-byte aligned.
+ *   - Every argument is validated before any HIP call; a failed check returns
+ *     a non-zero status and queues no work.  Nothing throws across the ABI.
+ *     svattn_last_error() gives a thread-local message for the last failure.
+ */
+#ifndef SVATTN_H
+#define SVATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SVATTN_API __attribute__((visibility("default")))
+#else
+#define SVATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVATTN_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+/* Status codes. */
+#define SVATTN_OK 0
+#define SVATTN_ERR_INVALID_ARG 1  /* null pointer, bad size, misalignment, aliasing */
+#define SVATTN_ERR_UNSUPPORTED 2  /* valid but not implemented (head_dim, tile size, kind/order) */
+#define SVATTN_ERR_HIP 3          /* HIP runtime or launch failure, including "no device" */
+
+/* Head kinds. */
+#define SVATTN_SPATIAL 0   /* keep iff |f_q - f_k| <= window, or f_k == 0 */
+#define SVATTN_TEMPORAL 1  /* keep iff max(|y_q-y_k|, |x_q-x_k|) <= radius, or f_k == 0 */
+#define SVATTN_DENSE 2     /* keep every pair (the dense comparator) */
+
+/* Token order a head's Q/K/V/O are stored in. */
+#define SVATTN_FRAME_MAJOR 0
+#define SVATTN_TEMPORAL_MAJOR 1   /* anchor-first; only for TEMPORAL and DENSE heads */
+
+/* Tile classes stored in svattn_tile_map.cls / col_cls. */
+#define SVATTN_TILE_EMPTY 0
+#define SVATTN_TILE_BOUNDARY 1
+#define SVATTN_TILE_FULL 2
+
+/* Flags for svattn_build_tile_map_ex. */
+#define SVATTN_MAP_ALL_BOUNDARY 1u  /* mark every non-empty tile BOUNDARY (the naive
+                                       traversal that masks every visited tile) */
+
+typedef struct {
+  int32_t frames, height, width; /* F, H, W >= 1; N = F*H*W < 2^31 / 256 */
+} svattn_geom;
+
+typedef struct {
+  int32_t kind;   /* SVATTN_SPATIAL / SVATTN_TEMPORAL / SVATTN_DENSE */
+  int32_t order;  /* SVATTN_FRAME_MAJOR / SVATTN_TEMPORAL_MAJOR */
+  int32_t window; /* spatial frame window w >= 0 (inclusive) */
+  int32_t radius; /* temporal Chebyshev patch radius r >= 0 (inclusive) */
+} svattn_mask;
+
+/*
+ * Tile map of one head layout: tile classes and, per q-tile, the ascending
+ * list of non-empty k-tiles (CSR).  Classes count only in-range pairs: EMPTY
+ * if no pair is kept, FULL if every in-range pair is kept, BOUNDARY otherwise.
+ * All four arrays are caller-owned device buffers:
+ *   cls     uint8 [n_qt * n_kt]   class of block (qt, kt) at qt*n_kt + kt
+ *   row_ptr int32 [n_qt + 1]      row_ptr[0] = 0, nnz = row_ptr[n_qt]
+ *   col     int32 [n_qt * n_kt]   capacity; entries [row_ptr[qt], row_ptr[qt+1])
+ *   col_cls uint8 [n_qt * n_kt]   class of each listed block (BOUNDARY or FULL)
+ * n_qt = ceil(N / block_q), n_kt = ceil(N / block_k) (svattn_tile_map_dims).
+ */
+typedef struct {
+  int32_t block_q, block_k, n_qt, n_kt;
+  uint8_t* cls;
+  int32_t* row_ptr;
+  int32_t* col;
+  uint8_t* col_cls;
+} svattn_tile_map;
+
+/* Host only.  n_qt / n_kt for a geometry and tile shape.
+ * block_q in {32, 64, 128, 256}, block_k in {32, 64, 128}. */
+SVATTN_API int svattn_tile_map_dims(const svattn_geom* geom, int32_t block_q, int32_t block_k,
+                         int32_t* n_qt, int32_t* n_kt);
+
+/*
+ * Tile classifier (the empty / full / boundary split of the aihirek.info page,
+ * section "A TPU-kernel kialakítása döntőnek bizonyult", paragraphs 2-3).
+ * Fills map->cls, row_ptr, col, col_cls for `mask` in `mask->order`.  Exact:
+ * classes are derived from the token coordinates of each block, not sampled.
+ * map->block_q/block_k/n_qt/n_kt must be set (n_qt/n_kt as from
+ * svattn_tile_map_dims).  The map depends only on (geom, mask, tile shape) and
+ * can be reused across calls.  Spatial heads must be FRAME_MAJOR.
+ */
+SVATTN_API int svattn_build_tile_map(const svattn_geom* geom, const svattn_mask* mask,
+                          svattn_tile_map* map, void* stream);
+SVATTN_API int svattn_build_tile_map_ex(const svattn_geom* geom, const svattn_mask* mask,
+                             svattn_tile_map* map, uint32_t flags, void* stream);
+
+/*
+ * Permutation index of the temporal-major order (ainews.tenesys.com, "Co się
+ * zmieniło?", item 5).  perm[t'] = frame-major token at temporal-major
+ * position t'; inv[t] = position of token t (inv may be NULL).  int32 [N].
+ */
+SVATTN_API int svattn_permutation_index(const svattn_geom* geom, int32_t* perm, int32_t* inv, void* stream);
+
+/*
+ * Reorder rows of a [heads, N, head_dim] bf16 tensor frame-major ->
+ * temporal-major (permute) or back (unpermute): dst[h, t', :] = src[h,
+ * perm[t'], :] and its inverse.  head_dim in {64, 128}.  src and dst must not
+ * overlap (no in-place).  Bit-exact row moves.
+ */
+SVATTN_API int svattn_permute_tokens(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                          const void* src, void* dst, void* stream);
+SVATTN_API int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                     const void* src, void* dst, void* stream);
+
+/*
+ * Block-sparse attention forward (aihirek.info, sections "A Sparse VideoGen a
+ * figyelmi fejeket osztályozza" and "A TPU-kernel kialakítása döntőnek
+ * bizonyult"): for every head h and query i,
+ *   O[h,i,:] = sum_j softmax_j(scales[h] * Q[h,i,:].K[h,j,:] over kept j) V[h,j,:]
+ * visiting only the k-tiles listed in maps[h]; FULL tiles run without a mask,
+ * BOUNDARY tiles (and the ragged last k-tile) evaluate the coordinate mask.
+ *   masks  host array [heads]: kind/order/window/radius of each head; Q/K/V/O
+ *          of head h are in masks[h].order
+ *   maps   host array [heads] of pointers to maps built for (geom, masks[h]);
+ *          heads may share a map; all maps share one (block_q, block_k) with
+ *          block_q in {32, 64, 128, 256} and block_k in {32, 64}
+ *   scales host array [heads], finite fp32 softmax scales > 0
+ *   lse    optional device fp32 [heads, N]: natural-log sum of exp of kept
+ *          scaled scores (NULL to skip)
+ * bf16 in, fp32 accumulation and softmax, bf16 out (round to nearest even).
+ * head_dim in {64, 128}.  o (and lse) must not overlap q, k or v.  The result
+ * does not depend on the order of heads or on which heads share a map.
+ */
+SVATTN_API int svattn_forward(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                              const svattn_mask* masks, const svattn_tile_map* const* maps,
+                              const float* scales, const void* q, const void* k, const void* v,
+                              void* o, float* lse, void* stream);
+
+/*
+ * Same as svattn_forward, with a separate device pointer per head instead of
+ * one [heads, N, head_dim] tensor: q[h], k[h], v[h], o[h] are [N, head_dim]
+ * bf16 (16-byte aligned), lse is NULL or a host array whose entries are NULL
+ * or fp32 [N].  Lets frame-major heads read the model's tensors in place
+ * while temporal heads read permuted copies.  No o[h] may overlap any input
+ * or another head's output.
+ */
+SVATTN_API int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                                   const svattn_mask* masks, const svattn_tile_map* const* maps,
+                                   const float* scales, const void* const* q, const void* const* k,
+                                   const void* const* v, void* const* o, float* const* lse,
+                                   void* stream);
+
+/*
+ * Reference forward for an arbitrary mask given as bits (for checking and
+ * debugging; it visits every tile and masks every pair).
+ *   mask_bits device uint32 [per_head ? heads : 1][n_tokens][ceil(n_tokens/32)]:
+ *             bit (j % 32) of word j / 32 of row i is 1 iff pair (i, j) is kept
+ *   A query row with no kept key gets O = 0 and lse = -inf.
+ * block_q in {32, 64, 128, 256}, block_k in {32, 64}; other arguments as for
+ * svattn_forward.
+ */
+SVATTN_API int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim,
+                              const uint32_t* mask_bits, int32_t per_head, const float* scales,
+                              const void* q, const void* k, const void* v, void* o, float* lse,
+                              int32_t block_q, int32_t block_k, void* stream);
+
+/* Static description of a status code. */
+SVATTN_API const char* svattn_status_string(int status);
+/* Thread-local detail of the last non-zero status returned on this thread. */
+SVATTN_API const char* svattn_last_error(void);
+/* SVATTN_VERSION of the loaded library. */
+SVATTN_API int svattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVATTN_H */

@@ -1,0 +1,185 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point the
+header declares, and rejects invalid arguments with the documented status
+before any HIP call.  No call here reaches a kernel launch: every call carries
+at least one invalid argument, except the no-device check, which only runs
+when the process sees no GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_sparse_spatio_svattn_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svattn.h")
+
+OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
+FAKE = 0x100000  # 16-byte-aligned stand-in address; never dereferenced here
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SVATTN_API\s+[\w\s\*]*?\b(svattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = sv.lib()
+    names = _declared()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(L, n), n
+    # and nothing else named svattn_ beyond the header
+    syms = os.popen(f"nm -D --defined-only {sv.LIB_PATH}").read()
+    exported = set(re.findall(r" T (svattn_\w+)", syms))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_version_and_status_strings():
+    assert sv.version() == 10000
+    L = sv.lib()
+    for code, name in [(0, b"SVATTN_OK"), (1, b"SVATTN_ERR_INVALID_ARG"), (2, b"SVATTN_ERR_UNSUPPORTED"),
+                       (3, b"SVATTN_ERR_HIP"), (99, b"SVATTN_ERR_UNKNOWN")]:
+        assert L.svattn_status_string(code) == name
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def _err():
+    return sv.lib().svattn_last_error().decode()
+
+
+def test_tile_map_dims_validation():
+    L = sv.lib()
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    g = sv.Geom(21, 45, 80)
+    assert L.svattn_tile_map_dims(ctypes.byref(g), 256, 64, ctypes.byref(a), ctypes.byref(b)) == OK
+    assert (a.value, b.value) == (296, 1182)
+    assert L.svattn_tile_map_dims(None, 256, 64, ctypes.byref(a), ctypes.byref(b)) == INVALID
+    assert "geom" in _err()
+    assert L.svattn_tile_map_dims(ctypes.byref(sv.Geom(0, 4, 4)), 32, 32, ctypes.byref(a), ctypes.byref(b)) == INVALID
+    assert L.svattn_tile_map_dims(ctypes.byref(g), 48, 64, ctypes.byref(a), ctypes.byref(b)) == UNSUPPORTED
+    assert L.svattn_tile_map_dims(ctypes.byref(g), 256, 256, ctypes.byref(a), ctypes.byref(b)) == UNSUPPORTED
+    assert L.svattn_tile_map_dims(ctypes.byref(sv.Geom(1024, 128, 256)), 256, 64, ctypes.byref(a),
+                                  ctypes.byref(b)) == UNSUPPORTED
+
+
+def _map(g, bq, bk, **kw):
+    n_qt, n_kt = -(-g.n // bq), -(-g.n // bk)
+    c = sv._TileMapC(bq, bk, n_qt, n_kt, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_build_tile_map_validation():
+    L = sv.lib()
+    g = sv.Geom(5, 24, 40)
+    good_mask = sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 2)
+    cases = [
+        (sv.Mask(7, 0, 0, 0), _map(g, 64, 64), 0, INVALID),                     # bad kind
+        (sv.Mask(0, 3, 0, 0), _map(g, 64, 64), 0, INVALID),                     # bad order
+        (sv.Mask(0, 0, -1, 0), _map(g, 64, 64), 0, INVALID),                    # negative window
+        (sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR, 1, 0), _map(g, 64, 64), 0, UNSUPPORTED),
+        (good_mask, _map(g, 96, 64), 0, UNSUPPORTED),                           # bad block_q
+        (good_mask, _map(g, 64, 64, n_qt=3), 0, INVALID),                       # wrong dims
+        (good_mask, _map(g, 64, 64, col=None), 0, INVALID),                     # NULL buffer
+        (good_mask, _map(g, 64, 64, row_ptr=FAKE + 2), 0, INVALID),             # misaligned
+        (good_mask, _map(g, 64, 64), 4, INVALID),                               # unknown flag
+    ]
+    for m, mp, flags, want in cases:
+        got = L.svattn_build_tile_map_ex(ctypes.byref(g), ctypes.byref(m), ctypes.byref(mp), flags, None)
+        assert got == want, (m, got, _err())
+
+
+def test_permute_validation():
+    L = sv.lib()
+    g = sv.Geom(4, 8, 8)
+    assert L.svattn_permute_tokens(ctypes.byref(g), 2, 96, FAKE, FAKE * 4, None) == UNSUPPORTED
+    assert L.svattn_permute_tokens(ctypes.byref(g), 0, 64, FAKE, FAKE * 4, None) == INVALID
+    assert L.svattn_permute_tokens(ctypes.byref(g), 2, 64, None, FAKE * 4, None) == INVALID
+    assert L.svattn_permute_tokens(ctypes.byref(g), 2, 64, FAKE + 8, FAKE * 4, None) == INVALID
+    assert L.svattn_unpermute(ctypes.byref(g), 2, 64, FAKE, FAKE + 64, None) == INVALID   # overlap
+    assert "overlap" in _err()
+    assert L.svattn_permutation_index(ctypes.byref(g), None, None, None) == INVALID
+    assert L.svattn_permutation_index(ctypes.byref(g), FAKE, FAKE + 4, None) == INVALID  # perm/inv overlap
+
+
+def _fwd(L, g, heads=2, d=128, masks=None, maps=None, scales=None, q=FAKE, k=FAKE * 16, v=FAKE * 32,
+         o=FAKE * 64, lse=None):
+    masks = masks or [sv.Mask(sv.SPATIAL, 0, 1, 0)] * heads
+    maps = maps or [_map(g, 256, 64)] * heads
+    scales = scales or [0.1] * heads
+    marr = (sv.Mask * heads)(*masks)
+    P = ctypes.POINTER(sv._TileMapC)
+    parr = (P * heads)(*[ctypes.pointer(m) for m in maps])
+    sarr = (ctypes.c_float * heads)(*scales)
+    return L.svattn_forward(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o, lse, None)
+
+
+def test_forward_validation():
+    L = sv.lib()
+    g = sv.Geom(4, 8, 8)   # N = 256
+    n_bytes = 2 * 256 * 128 * 2
+    assert _fwd(L, g, d=96) == UNSUPPORTED
+    assert _fwd(L, g, scales=[0.1, 0.0]) == INVALID
+    assert _fwd(L, g, scales=[0.1, float("nan")]) == INVALID
+    assert _fwd(L, g, q=None) == INVALID
+    assert _fwd(L, g, k=FAKE * 16 + 4) == INVALID                            # misaligned
+    assert _fwd(L, g, o=FAKE + n_bytes // 2) == INVALID                      # o overlaps q
+    assert "overlap" in _err()
+    assert _fwd(L, g, lse=FAKE * 64 + 16) == INVALID                         # lse overlaps o
+    assert _fwd(L, g, maps=[_map(g, 256, 64), _map(g, 128, 64)]) == INVALID  # mixed tiles
+    assert _fwd(L, g, maps=[_map(g, 256, 128)] * 2) == UNSUPPORTED           # block_k 128
+    assert _fwd(L, g, maps=[_map(g, 256, 64, n_kt=5)] * 2) == INVALID
+    assert _fwd(L, g, maps=[_map(g, 256, 64, col_cls=None)] * 2) == INVALID
+    assert _fwd(L, g, masks=[sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR, 1, 0)] * 2) == UNSUPPORTED
+    assert L.svattn_forward(ctypes.byref(g), 2, 128, None, None, None, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+
+
+def test_forward_ptrs_and_dense_mask_validation():
+    L = sv.lib()
+    g = sv.Geom(4, 8, 8)
+    heads, d = 2, 64
+    hb = 256 * d * 2
+    marr = (sv.Mask * heads)(*[sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 1)] * heads)
+    m = _map(g, 64, 32)
+    P = ctypes.POINTER(sv._TileMapC)
+    parr = (P * heads)(ctypes.pointer(m), ctypes.pointer(m))
+    sarr = (ctypes.c_float * heads)(0.1, 0.1)
+    VP = ctypes.c_void_p * heads
+    q, k, v = VP(FAKE, FAKE + hb), VP(FAKE * 16, FAKE * 16 + hb), VP(FAKE * 32, FAKE * 32 + hb)
+    o_overlap = VP(FAKE * 64, FAKE * 64 + 16)                # two heads' outputs overlap
+    assert L.svattn_forward_ptrs(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o_overlap, None,
+                                 None) == INVALID
+    o_in = VP(FAKE * 64, FAKE + hb)                           # head 1 writes over q of head 1
+    assert L.svattn_forward_ptrs(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o_in, None,
+                                 None) == INVALID
+    assert L.svattn_forward_ptrs(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, None, None,
+                                 None) == INVALID
+    # dense-mask entry
+    assert L.svattn_forward_dense_mask(2, 0, 64, FAKE, 1, sarr, FAKE, FAKE * 16, FAKE * 32, FAKE * 64, None,
+                                       64, 32, None) == INVALID
+    assert L.svattn_forward_dense_mask(2, 256, 64, None, 1, sarr, FAKE, FAKE * 16, FAKE * 32, FAKE * 64, None,
+                                       64, 32, None) == INVALID
+    assert L.svattn_forward_dense_mask(2, 256, 64, FAKE * 128, 1, sarr, FAKE, FAKE * 16, FAKE * 32, FAKE * 64,
+                                       None, 64, 128, None) == UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    g = sv.Geom(4, 8, 8)
+    x = torch.zeros(1, 256, 64, dtype=torch.bfloat16)
+    with pytest.raises(sv.SvattnError):
+        sv.permute_tokens(g, x, out=torch.zeros_like(x))
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device error path")
+def test_valid_call_without_device_reports_hip_error():
+    L = sv.lib()
+    g = sv.Geom(4, 8, 8)
+    st = L.svattn_permutation_index(ctypes.byref(g), FAKE, None, None)
+    assert st == HIP
+    assert len(_err()) > 0

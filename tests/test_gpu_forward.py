@@ -1,0 +1,219 @@
+"""GPU parity of the attention forward against the fp64 oracle.
+
+Bar (bf16 output vs fp64 oracle): max-abs <= 2e-2 and mean-abs <= 2e-3 over
+the compared outputs.  Small shapes compare every output; the full-size
+workloads compare seeded sampled query rows, in the launch configuration the
+benchmark times (block 256 x 64, temporal heads temporal-major through the
+permute -> forward -> unpermute path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import svattn_synth as synth
+from _util import assert_close, bits_of, f64_of, sv_mask, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import block_sparse_spatio_svattn_amd as m
+    return m
+
+
+def _oracle_rows(wl, inp, rows_per_head):
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+    out = []
+    for h, head in enumerate(wl.heads):
+        o, lse = oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind,
+                                    head.window, head.radius, rows=rows_per_head[h])
+        out.append((o, lse))
+    return out
+
+
+def _run_layer(sv, wl, inp, bq, bk, orders=None, flags=0):
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    masks = [sv_mask(h, None if orders is None else orders[i]) for i, h in enumerate(wl.heads)]
+    layer = SparseVideoAttention(g, masks, wl.head_dim, bq, bk, map_flags=flags)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    o = layer(q, k, v, [float(s) for s in inp.scales])
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("bq,bk", [(32, 32), (64, 32), (32, 64), (256, 64), (128, 64)])
+@pytest.mark.parametrize("order", ["fm", "tm"])
+def test_tiny_all_rows(sv, bq, bk, order):
+    wl = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, bq, bk, orders=["fm", order])
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"tiny h{h} {order} {bq}x{bk}")
+
+
+@pytest.mark.parametrize("bq,bk", [(64, 64), (128, 64), (256, 64), (256, 32), (128, 32)])
+def test_small_all_rows(sv, bq, bk):
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, bq, bk)
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"small h{h} {bq}x{bk}")
+
+
+def test_small_lse_and_direct_entry(sv):
+    """svattn_forward on layout tensors (frame-major heads only) incl. lse."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    masks = [sv_mask(h, "fm") for h in wl.heads]
+    maps = [sv.build_tile_map(g, m, 256, 64) for m in masks]
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    lse = torch.empty(wl.n_heads, wl.n_tokens, dtype=torch.float32, device="cuda")
+    o = sv.forward(g, q, k, v, masks, maps, [float(s) for s in inp.scales], lse=lse)
+    torch.cuda.synchronize()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"small direct h{h}")
+        dl = np.abs(lse[h].cpu().numpy().astype(np.float64) - ref[h][1]).max()
+        assert dl < 1e-3, dl
+
+
+@pytest.mark.parametrize("wl_name", ["headline", "perm_study", "p1440"])
+def test_full_size_sampled_rows(sv, wl_name):
+    wl = synth.WORKLOADS[wl_name]
+    inp = synth.make_inputs(wl)
+    rows = synth.sample_rows(wl, min(wl.sample_rows, 256))
+    print(f"{wl_name}: N={wl.n_tokens} heads={wl.n_heads} rows/head={rows.shape[1]}", flush=True)
+    o = _run_layer(sv, wl, inp, 256, 64)
+    ref = _oracle_rows(wl, inp, rows)
+    got = np.stack([f64_of(o[h][torch.from_numpy(rows[h]).cuda()]) for h in range(wl.n_heads)])
+    assert_close(got, np.stack([r[0] for r in ref]), f"{wl_name} sampled rows")
+
+
+def test_perm_study_frame_major_order(sv):
+    wl = synth.WORKLOADS["perm_study"]
+    inp = synth.make_inputs(wl)
+    rows = synth.sample_rows(wl, 64)
+    o = _run_layer(sv, wl, inp, 256, 64, orders=["fm"] * wl.n_heads)
+    ref = _oracle_rows(wl, inp, rows)
+    got = np.stack([f64_of(o[h][torch.from_numpy(rows[h]).cuda()]) for h in range(wl.n_heads)])
+    assert_close(got, np.stack([r[0] for r in ref]), "perm_study frame-major")
+
+
+@pytest.mark.slow
+def test_p1440_2048_rows(sv):
+    wl = synth.WORKLOADS["p1440"]
+    inp = synth.make_inputs(wl)
+    rows = synth.sample_rows(wl)
+    o = _run_layer(sv, wl, inp, 256, 64)
+    ref = _oracle_rows(wl, inp, rows)
+    got = np.stack([f64_of(o[h][torch.from_numpy(rows[h]).cuda()]) for h in range(wl.n_heads)])
+    assert_close(got, np.stack([r[0] for r in ref]), "p1440 2048 rows/head")
+
+
+def test_dense_kind_and_all_boundary_bit_identical(sv):
+    """DENSE heads equal the oracle's dense attention; a map with every tile
+    marked BOUNDARY gives bit-identical outputs to the normal map."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    o1 = _run_layer(sv, wl, inp, 256, 64)
+    o2 = _run_layer(sv, wl, inp, 256, 64, flags=sv.MAP_ALL_BOUNDARY)
+    assert (bits_of(o1) == bits_of(o2)).all()
+    dwl = wl.with_heads([synth.Head("dense")] * 2)
+    dinp = synth.make_inputs(dwl)
+    od = _run_layer(sv, dwl, dinp, 256, 64)
+    ref = _oracle_rows(dwl, dinp, [np.arange(dwl.n_tokens)] * 2)
+    for h in range(2):
+        assert_close(f64_of(od[h]), ref[h][0], f"dense h{h}")
+
+
+def test_deterministic_and_head_order_invariant(sv):
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    o1 = bits_of(_run_layer(sv, wl, inp, 256, 64))
+    o2 = bits_of(_run_layer(sv, wl, inp, 256, 64))
+    assert (o1 == o2).all()
+    rev = wl.with_heads(list(reversed(wl.heads)))
+    rinp = synth.Inputs(q=inp.q[::-1].copy(), k=inp.k[::-1].copy(), v=inp.v[::-1].copy(),
+                        scales=inp.scales[::-1].copy(), multipliers=inp.multipliers[::-1].copy())
+    o3 = bits_of(_run_layer(sv, rev, rinp, 256, 64))
+    assert (o3[::-1] == o1).all()
+
+
+@pytest.mark.parametrize("geom,heads,bq,bk", [
+    ((3, 5, 7), [synth.Head("temporal", radius=1, order="tm"), synth.Head("spatial", window=0)], 64, 32),
+    ((3, 5, 7), [synth.Head("temporal", radius=0, order="fm"), synth.Head("spatial", window=1)], 32, 64),
+    ((1, 8, 8), [synth.Head("temporal", radius=1, order="tm"), synth.Head("spatial", window=0)], 32, 32),
+    ((2, 3, 5), [synth.Head("temporal", radius=3, order="tm"), synth.Head("dense")], 256, 64),
+    ((9, 1, 3), [synth.Head("temporal", radius=0, order="tm"), synth.Head("spatial", window=2)], 64, 64),
+])
+def test_edge_geometries(sv, geom, heads, bq, bk):
+    """Ragged tails (N not a multiple of either tile), a single frame (every key is
+    an anchor), N smaller than one tile, zero windows, and dense heads."""
+    F, H, W = geom
+    wl = synth.Workload(name="edge", seed=77, frames=F, height=H, width=W, head_dim=64,
+                        heads=tuple(heads), tiles=((bq, bk),))
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, bq, bk)
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"edge {geom} h{h}")
+
+
+def _bits_from_keep(keep):
+    n = keep.shape[-1]
+    words = (n + 31) // 32
+    pad = np.zeros(keep.shape[:-1] + (words * 32,), dtype=bool)
+    pad[..., :n] = keep
+    b = pad.reshape(keep.shape[:-1] + (words, 32)).astype(np.uint64)
+    w = (b << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
+    return torch.from_numpy(w.view(np.int32)).cuda()
+
+
+@pytest.mark.parametrize("n,d,bq,bk", [(200, 64, 64, 32), (333, 128, 128, 64), (96, 128, 32, 64)])
+def test_dense_mask_entry_random_bits(sv, n, d, bq, bk):
+    heads = 2
+    q = synth.random_bf16((heads, n, d), 5)
+    k = synth.random_bf16((heads, n, d), 6)
+    v = synth.random_bf16((heads, n, d), 7)
+    keep = synth.random_bits((heads, n, n), 8, density=0.3)
+    keep[0, 3, :] = False          # a row with no kept key: O = 0, lse = -inf
+    keep[1, :, 0] = True
+    scales = [0.1, 0.2]
+    lse = torch.empty(heads, n, dtype=torch.float32, device="cuda")
+    o = sv.forward_dense_mask(to_dev(q), to_dev(k), to_dev(v), _bits_from_keep(keep), scales,
+                              per_head=True, block_q=bq, block_k=bk, lse=lse)
+    torch.cuda.synchronize()
+    for h in range(heads):
+        live = keep[h].any(1)
+        ref, rl = oracle.attend_rows(oracle.bf16_to_f64(q[h][live]), oracle.bf16_to_f64(k[h]),
+                                     oracle.bf16_to_f64(v[h]), float(np.float32(scales[h])), keep[h][live])
+        got = f64_of(o[h])
+        assert_close(got[live], ref, f"dense-mask h{h}")
+        assert (got[~live] == 0).all()
+        lh = lse[h].cpu().numpy()
+        assert np.isneginf(lh[~live]).all()
+        assert np.abs(lh[live] - rl).max() < 1e-3
+
+
+def test_dense_mask_entry_matches_coordinate_masks(sv):
+    """The bit-mask reference path with the oracle's spatial/temporal masks agrees
+    with the coordinate-mask path (both within the parity bar of the oracle)."""
+    wl = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(wl)
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+    keep = np.stack([oracle.keep_matrix(g, h.kind, h.window, h.radius, np.arange(g.n), np.arange(g.n))
+                     for h in wl.heads])
+    o = sv.forward_dense_mask(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), _bits_from_keep(keep),
+                              [float(s) for s in inp.scales], per_head=True, block_q=64, block_k=32)
+    o2 = _run_layer(sv, wl, inp, 64, 32, orders=["fm", "fm"])
+    torch.cuda.synchronize()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * 2)
+    for h in range(2):
+        assert_close(f64_of(o[h]), ref[h][0], f"bits h{h}")
+        assert (bits_of(o[h]) == bits_of(o2[h])).all()

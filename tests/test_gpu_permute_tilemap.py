@@ -1,0 +1,121 @@
+"""GPU parity: permutation index, token permutation and tile maps must match the
+oracle bit-exactly (integer and byte work)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import svattn_synth as synth
+from _util import bits_of, sv_mask, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GEOMS = [(4, 8, 8), (5, 24, 40), (21, 45, 80), (21, 90, 160), (3, 5, 7), (1, 4, 4), (2, 3, 5), (7, 1, 9)]
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import block_sparse_spatio_svattn_amd as m
+    return m
+
+
+@pytest.mark.parametrize("F,H,W", GEOMS)
+def test_permutation_index_bit_exact(sv, F, H, W):
+    g = sv.Geom(F, H, W)
+    perm, inv = sv.permutation_index(g)
+    ref = oracle.temporal_major_perm(oracle.Geometry(F, H, W))
+    p = perm.cpu().numpy()
+    assert (p == ref).all()
+    iv = inv.cpu().numpy()
+    assert (iv[ref] == np.arange(g.n)).all()
+
+
+@pytest.mark.parametrize("F,H,W,d,heads", [(4, 8, 8, 64, 2), (5, 24, 40, 128, 3), (3, 5, 7, 128, 2),
+                                           (21, 45, 80, 128, 5), (1, 4, 4, 64, 1)])
+def test_permute_unpermute_bit_exact(sv, F, H, W, d, heads):
+    g = sv.Geom(F, H, W)
+    x = synth.random_bf16((heads, g.n, d), seed=F * 1000 + W)
+    xd = to_dev(x)
+    perm = oracle.temporal_major_perm(oracle.Geometry(F, H, W))
+    y = sv.permute_tokens(g, xd)
+    torch.cuda.synchronize()
+    assert (bits_of(y) == x[:, perm]).all()
+    back = sv.unpermute(g, y)
+    torch.cuda.synchronize()
+    assert (bits_of(back) == x).all()
+
+
+def _compare_map(m, ref, qtiles=None):
+    cls_ref, rp_ref, col_ref, cc_ref = ref
+    cls = m.cls.cpu().numpy().reshape(m.n_qt, m.n_kt)
+    rp = m.row_ptr.cpu().numpy()
+    col = m.col.cpu().numpy()
+    cc = m.col_cls.cpu().numpy()
+    rows = range(m.n_qt) if qtiles is None else qtiles
+    for i, qt in enumerate(rows):
+        assert (cls[qt] == cls_ref[i]).all(), f"cls row {qt}"
+        a, b = rp[qt], rp[qt + 1]
+        ra, rb = rp_ref[i], rp_ref[i + 1]
+        assert b - a == rb - ra, f"row {qt} nnz"
+        assert (col[a:b] == col_ref[ra:rb]).all(), f"col row {qt}"
+        assert (cc[a:b] == cc_ref[ra:rb]).all(), f"col_cls row {qt}"
+    # whole-map invariants
+    assert rp[0] == 0 and (np.diff(rp) >= 0).all()
+    assert rp[-1] == int((cls != 0).sum())
+    nz_cols = col[:rp[-1]]
+    for qt in range(m.n_qt):
+        seg = nz_cols[rp[qt]:rp[qt + 1]]
+        assert (np.diff(seg) > 0).all()
+    assert (cc[:rp[-1]] == cls[np.repeat(np.arange(m.n_qt), np.diff(rp)), nz_cols]).all()
+
+
+SMALL_CASES = (
+    [((4, 8, 8), k, w, r, o, bq, bk) for (k, w, r, o) in
+     [("spatial", 1, 0, "fm"), ("temporal", 0, 1, "fm"), ("temporal", 0, 1, "tm"), ("dense", 0, 0, "fm"),
+      ("temporal", 0, 0, "tm"), ("spatial", 0, 0, "fm")]
+     for bq in (32, 64, 256) for bk in (32, 64, 128)]
+    + [((5, 24, 40), k, w, r, o, bq, bk) for (k, w, r, o) in
+       [("spatial", 1, 0, "fm"), ("temporal", 0, 2, "fm"), ("temporal", 0, 2, "tm")]
+       for bq in (64, 128, 256) for bk in (32, 64, 128)]
+    + [((3, 5, 7), "temporal", 0, 1, "tm", 32, 32), ((3, 5, 7), "spatial", 1, 0, "fm", 64, 32),
+       ((1, 4, 4), "temporal", 0, 1, "tm", 32, 32), ((7, 1, 9), "temporal", 0, 2, "tm", 32, 64),
+       ((2, 3, 5), "spatial", 0, 0, "fm", 32, 128)]
+)
+
+
+@pytest.mark.parametrize("geom,kind,w,r,order,bq,bk", SMALL_CASES)
+def test_tile_map_bit_exact(sv, geom, kind, w, r, order, bq, bk):
+    g = sv.Geom(*geom)
+    head = synth.Head(kind, window=w, radius=r, order=order)
+    m = sv.build_tile_map(g, sv_mask(head), bq, bk)
+    torch.cuda.synchronize()
+    ref = oracle.tile_map(oracle.Geometry(*geom), kind, w, r, order, bq, bk)
+    _compare_map(m, ref)
+
+
+@pytest.mark.parametrize("wl_name,hi,order", [("headline", 0, "fm"), ("headline", 5, "tm"),
+                                              ("headline", 5, "fm"), ("perm_study", 0, "tm"),
+                                              ("p1440", 0, "fm"), ("p1440", 5, "tm")])
+@pytest.mark.parametrize("bq,bk", [(256, 64), (128, 32)])
+def test_tile_map_large_sampled_rows(sv, wl_name, hi, order, bq, bk):
+    wl = synth.WORKLOADS[wl_name]
+    h = wl.heads[hi]
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    m = sv.build_tile_map(g, sv_mask(h, order), bq, bk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(hi + bq)
+    qtiles = sorted(set([0, m.n_qt - 1] + list(rng.choice(m.n_qt, 4, replace=False))))
+    ref = oracle.tile_map(oracle.Geometry(wl.frames, wl.height, wl.width), h.kind, h.window, h.radius,
+                          order, bq, bk, qtiles=qtiles)
+    _compare_map(m, ref, qtiles)
+
+
+def test_all_boundary_flag(sv):
+    g = sv.Geom(5, 24, 40)
+    mk = sv_mask(synth.Head("temporal", radius=2, order="tm"))
+    a = sv.build_tile_map(g, mk, 128, 64)
+    b = sv.build_tile_map(g, mk, 128, 64, flags=sv.MAP_ALL_BOUNDARY)
+    torch.cuda.synchronize()
+    ca, cb = a.cls.cpu().numpy(), b.cls.cpu().numpy()
+    assert ((ca != 0) == (cb != 0)).all() and set(np.unique(cb)) <= {0, 1}
+    assert (a.row_ptr.cpu().numpy() == b.row_ptr.cpu().numpy()).all()
