@@ -246,9 +246,13 @@ def cpu_baseline(wl, inp, seconds):
                                                                      rows[h]).sum())
         return dt, fl
 
-    dt, fl = run(8)
-    r = int(max(8, min(4096, 8 * seconds / max(dt, 1e-3))))
-    dt, fl = run(r)
+    rows, dt = 32, 0.0
+    while True:  # grow the sample until it costs about `seconds`
+        dt, fl = run(rows)
+        if dt >= 0.5 * seconds or rows >= 4096:
+            break
+        rows = int(min(4096, max(2 * rows, rows * 0.7 * seconds / max(dt, 1e-3))))
+    r = rows
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{r} seeded query rows per head x {wl.n_heads} heads of {wl.n_tokens}, fp64 numpy, "
                       f"{dt:.1f} s wall", "seconds": round(dt, 2)}

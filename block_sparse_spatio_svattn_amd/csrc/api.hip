@@ -13,8 +13,10 @@
 #include "internal.hpp"
 
 namespace svattn {
-hipError_t launch_forward_d64(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
-hipError_t launch_forward_d128(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
+hipError_t launch_forward_d64_map(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
+hipError_t launch_forward_d128_map(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
+hipError_t launch_forward_d64_bits(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
+hipError_t launch_forward_d128_bits(const FwdArgs& a, int block_q, int block_k, hipStream_t st);
 }  // namespace svattn
 
 using namespace svattn;
@@ -98,7 +100,9 @@ int check_map_buffers(const svattn_tile_map* map, const char* who) {
 }
 
 hipError_t dispatch_forward(const FwdArgs& a, int head_dim, int bq, int bk, hipStream_t st) {
-  return head_dim == 128 ? launch_forward_d128(a, bq, bk, st) : launch_forward_d64(a, bq, bk, st);
+  if (a.dense_bits)
+    return head_dim == 128 ? launch_forward_d128_bits(a, bq, bk, st) : launch_forward_d64_bits(a, bq, bk, st);
+  return head_dim == 128 ? launch_forward_d128_map(a, bq, bk, st) : launch_forward_d64_map(a, bq, bk, st);
 }
 
 }  // namespace
@@ -305,6 +309,8 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
     if (m->n_qt != cdiv(n, bq) || m->n_kt != cdiv(n, bk))
       return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] dims %d x %d do not match the geometry", h, m->n_qt, m->n_kt);
     if (!m->row_ptr || !m->col || !m->col_cls) return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] buffer is NULL", h);
+    if (!aligned(m->row_ptr, 4) || !aligned(m->col, 4) || !aligned(m->col_cls, 4))
+      return fail(SVATTN_ERR_INVALID_ARG, "maps[%d]: row_ptr, col and col_cls must be 4-byte aligned", h);
   }
   if ((s = check_ptrs(ptrs, n, head_dim))) return s;
 

@@ -1,0 +1,510 @@
+// Block-sparse flash-attention forward for gfx950 (CDNA4), bf16 MFMA,
+// software-pipelined.
+//
+// What it computes ("Accelerating Spatio-Temporal Attention for Video
+// Diffusion on TPUs", aihirek.info): softmax attention restricted to the kept
+// query-key pairs of a spatial or temporal head with a first-frame anchor
+// (section "A Sparse VideoGen a figyelmi fejeket osztályozza", paragraphs 2-3),
+// visiting only the non-empty tiles of the tile map, with a mask-free path for
+// full tiles and coordinate masking only on boundary tiles and on the ragged
+// last k-tile (section "A TPU-kernel kialakítása döntőnek bizonyult",
+// paragraphs 2-3).
+//
+// Work decomposition.  One workgroup owns one (head, q-tile) of
+// BQ = NW * QG * 32 queries; each of its NW waves owns QG groups of 32
+// queries and keeps their Q fragments in registers.  The workgroup walks the
+// q-tile's list of non-empty k-tiles.  K and V tiles (BK keys each) go from
+// HBM straight into an LDS ring of STAGES stages with global_load_lds_dwordx4
+// (each lane's 16 bytes land at the wave's LDS base + 16 * lane), so no
+// registers hold staged tiles.
+//
+// Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
+// lane l holds query l % 32 and 16 of the 32 keys of a key block, so a
+// query's running max and sum stay inside the lane pair (l, l ^ 32).  The
+// same registers, rounded to bf16, are the B operand of O^T += V^T P^T.  The A
+// operand V^T is read from the row-major V tile with ds_read_b64_tr_b16: in
+// each 16-lane group, lane j receives element j % 4 of the 8-byte rows read by
+// lanes 4t + (j % 16) / 4, t = 0..3, i.e. four consecutive keys of one
+// dimension.  Two such reads give the eight keys a lane's P fragment holds.
+//
+// LDS layout.  K and V tiles are row-major (one key per row, D bf16).  K rows
+// are padded to 2D + 16 bytes, so the 16-byte reads of 16 consecutive keys
+// start 4 banks apart (the DMA fills the padding slots with a harmless copy
+// of a valid chunk).  V rows are unpadded and their 16-byte chunks are XOR
+// swizzled by the row (vswz): a transpose read covers rows 4a..4a+3, and the
+// swizzle gives each of those rows its own banks.
+//
+// Pipelining (STAGES == 3).  Iteration j computes S of tile j+1 on the MFMA
+// pipe while the VALU runs the softmax of tile j, then P V of tile j; the
+// loads of tile j+2 are in flight meanwhile.  A single barrier per iteration
+// suffices: the stage written at the end of iteration j held tile j-1, whose
+// last reader (P V of iteration j-1) finished before that barrier.
+// STAGES == 2 is the plain double-buffered loop.
+//
+// Softmax.  exp2 with the scale folded into one FMA; masked scores are -inf.
+// The running max only moves when a new score exceeds it by more than 8 in
+// log2 units, so most tiles skip rescaling the accumulator; the result differs
+// only by rounding.  P is rounded to bf16 for the P V product; the row sum
+// (and so lse) accumulates the fp32 values.
+#pragma once
+
+#include "internal.hpp"
+
+namespace svattn {
+namespace fwd2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+template <int D, int BK, int NW, int QG, int STAGES>
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BQ = NW * QG * 32;
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int RBK = D * 2 + 16;                  // K row stride in LDS (bytes)
+  static constexpr int RBV = D * 2;                       // V row stride in LDS (bytes)
+  static constexpr int K_PIECES = (BK * RBK + 1023) / 1024;  // 1 KB DMA pieces
+  static constexpr int V_PIECES = (BK * RBV + 1023) / 1024;
+  static constexpr int K_BYTES = K_PIECES * 1024;         // K region of a stage
+  static constexpr int STAGE_BYTES = (K_PIECES + V_PIECES) * 1024;
+  static constexpr int KB = BK / 32;                      // 32-key blocks per tile
+  static constexpr int DS = D / 16;                       // 16-dim MFMA steps of Q K^T
+  static constexpr int DB = D / 32;                       // 32-dim blocks of O
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kNegBig = -1.0e30f;        // initial running max (finite)
+
+// XOR applied to the chunk index of V row r (an involution for a fixed row).
+// Rows 4a..4a+3 map a 64-byte run of chunks to four distinct quarters of a
+// 256-byte bank window and a 32-byte run to four distinct quarters of a
+// 128-byte window (with 128-byte rows, D = 64, the row parity already picks
+// the half of the 256-byte window).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) + 2 * ((r >> 1) & 1) : 2 * (r & 3);
+}
+
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Load through the constant address space: a wave-uniform address becomes a
+// scalar load even after the tile copies' inline asm, which the compiler must
+// treat as a possible memory write.  Used only for the tile map, which no
+// kernel writes while the forward runs.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Packed patch coordinates (y << 16 | x) of a key position, or a far-away
+// value for positions >= N.
+__device__ __forceinline__ int key_coord(const Geo& g, int order, int key) {
+  if (key >= g.N) return 0x7fff7fff;
+  const int p = patch_of(g, order, key);
+  const int y = (int)g.divW.div((uint32_t)p);
+  return (y << 16) | (p - y * g.W);
+}
+
+template <int D, int BK, int NW, int QG, int STAGES, bool BITS>
+__global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
+  using C = Cfg<D, BK, NW, QG, STAGES>;
+  static_assert(BK % 32 == 0 && (D == 64 || D == 128), "tile shape");
+  static_assert(STAGES == 2 || STAGES == 3, "stages");
+  __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
+
+  // ---- work item: XCD-aware order (workgroup b runs on XCD b % 8) ----
+  const int b = blockIdx.x;
+  const int xcd = b & 7, s = b >> 3;
+  const int item = ((s / a.chunk) * 8 + xcd) * a.chunk + (s % a.chunk);
+  if (item >= a.n_items) return;
+  const int slot = item / a.n_qt;
+  const int qt = item - slot * a.n_qt;
+  const HeadDesc& hd = a.heads[slot];
+  const Geo g = a.g;
+  const int N = g.N;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
+  const __bf16* __restrict__ Q = (const __bf16*)hd.q;
+  const __bf16* __restrict__ K = (const __bf16*)hd.k;
+  const __bf16* __restrict__ V = (const __bf16*)hd.v;
+  const int q0 = qt * C::BQ + wave * (QG * 32);
+  const int kind = hd.kind, order = hd.order;
+
+  // ---- Q fragments (B operand of S^T = K Q^T); rows past N are clamped ----
+  bf16x8 qf[QG][C::DS];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    const int qi = min(q0 + gq * 32 + l32, N - 1);
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) qf[gq][ds] = *(const bf16x8*)(Q + (size_t)qi * D + ds * 16 + hh * 8);
+  }
+  // Wait for Q here: the compiler then knows no load of its own is pending
+  // in the loop, where the vector-memory counter belongs to the tile copies.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  // ---- per-query mask parameters ----
+  // spatial: kept non-anchor keys are [mq_a, mq_a + mq_b); temporal: patch (y, x)
+  int mq_a[QG], mq_b[QG];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    const int qi = min(q0 + gq * 32 + l32, N - 1);
+    if (kind == SVATTN_SPATIAL) {
+      const int f = (int)g.divP.div((uint32_t)qi);
+      const int flo = max(0, f - hd.window), fhi = min(g.F, f + hd.window + 1);
+      mq_a[gq] = flo * g.P;
+      mq_b[gq] = (fhi - flo) * g.P;
+    } else {
+      const int p = patch_of(g, order, qi);
+      const int y = (int)g.divW.div((uint32_t)p);
+      mq_a[gq] = y;
+      mq_b[gq] = p - y * g.W;
+    }
+  }
+
+  // ---- lane-constant LDS offsets ----
+  // K (A operand of S^T): row kb*32 + l32, bytes 32*ds + 16*hh.
+  const int koff = l32 * C::RBK + hh * 16;
+  // V (transpose reads): 16-lane group G = lane / 16, i = lane % 16 reads row
+  // 4*(G / 2) + i / 4 (+ 8 for the second read; rows are 4k + i / 4, so the
+  // swizzle only depends on i), 8 bytes at dims 32*db + 16*(G % 2) + 4*(i % 4).
+  const int G = lane >> 4, gi = lane & 15;
+  const int vsw = vswz<D>(gi >> 2);
+  int voff[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const int chunk = 4 * db + 2 * (G & 1) + ((gi & 3) >> 1);
+    voff[db] = (4 * (G >> 1) + (gi >> 2)) * C::RBV + ((chunk ^ vsw) << 4) + ((gi & 1) << 3);
+  }
+
+  floatx16 acc[QG][C::DB];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[gq][db] = floatx16{};
+  float m_run[QG], l_run[QG];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    m_run[gq] = kNegBig;
+    l_run[gq] = 0.f;
+  }
+  const float c = hd.scale_log2;
+  const bool need_kc = kind == SVATTN_TEMPORAL;
+
+  // Tile list: the map's CSR row; with a bit mask, every k-tile.
+  const int e0 = BITS ? 0 : ld_const(hd.row_ptr + qt);
+  const int n = BITS ? a.n_kt : ld_const(hd.row_ptr + qt + 1) - e0;
+
+  const int cap = a.n_qt * a.n_kt;  // capacity of col / col_cls
+  const uint8_t* __restrict__ col_cls = hd.col_cls;
+  const int32_t* __restrict__ col = hd.col + e0;
+  // First key of list entry j.
+  auto tile_key0 = [&](int j) -> int {
+    if constexpr (BITS) return j * BK;
+    else return ld_const(col + j) * BK;
+  };
+  // Bit-mask rows of this lane's queries (bit j % 32 of word j / 32: pair kept).
+  const uint32_t* bits_row[QG];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq)
+    bits_row[gq] = BITS ? hd.bits + (size_t)min(q0 + gq * 32 + l32, N - 1) * a.words_per_row : nullptr;
+
+  // Class of list entry e0 + j, read with a scalar load of its aligned
+  // 4-byte word (col_cls is 4-byte aligned); a byte read serves the last
+  // partial word of the buffer.
+  auto tile_class = [&](int j) -> int {
+    if constexpr (BITS) return SVATTN_TILE_BOUNDARY;
+    const int e = e0 + j;
+    if ((e | 3) < cap) {
+      const uint32_t w = ld_const((const uint32_t*)(col_cls + (e & ~3)));
+      return (int)((w >> ((e & 3) * 8)) & 0xffu);
+    }
+    return __builtin_amdgcn_readfirstlane((int)col_cls[e]);
+  };
+
+  // Issue the HBM -> LDS copies of K and V tile `key0` into stage st, and the
+  // key coordinates of temporal heads.  Wave w copies the 1 KB pieces
+  // w, w + NW, ... of the stage; lane L of a piece fills byte 16 L of it, i.e.
+  // one 16-byte chunk slot of a padded row, and fetches that chunk of the
+  // key's row (padding slots fetch the tile's first chunk).  The copies are
+  // issued as inline asm so that the compiler inserts no wait for them before
+  // the LDS reads of other stages; wait_tiles() waits for them.
+  auto issue = [&](int key0, int st) {
+    const uint32_t stage_lds = lds_base + st * C::STAGE_BYTES;
+    constexpr int OPS = C::K_PIECES + C::V_PIECES;
+    const int first = min(key0, N - 1) * D;
+#pragma unroll
+    for (int i = 0; i < (OPS + NW - 1) / NW; ++i) {
+      const int o = wave_u + i * NW;
+      if (OPS % NW != 0 && o >= OPS) break;
+      const bool is_k = o < C::K_PIECES;
+      const int byte = (is_k ? o : o - C::K_PIECES) * 1024 + lane * 16;
+      const int rb = is_k ? C::RBK : C::RBV;
+      const int row = byte / rb, slot = (byte - row * rb) >> 4;
+      const int chunk = is_k ? slot : (slot ^ vswz<D>(row));
+      const int off = (row < BK && slot < C::CPR) ? min(key0 + row, N - 1) * D + chunk * 8  // rows past N are masked
+                                                  : first;
+      const __bf16* src = (is_k ? K : V) + off;
+      const uint32_t dst = stage_lds + o * 1024;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+    }
+    if (need_kc && tid < BK) kcs[st][tid] = fwd2::key_coord(g, order, key0 + tid);
+  };
+  // All of this wave's copies have landed in LDS (the barrier that follows
+  // makes every wave's copies visible).
+  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // S^T = K Q^T for the tile in stage st.
+  auto qk = [&](int st, floatx16 (&S)[C::KB][QG]) {
+    const char* Ks = smem + st * C::STAGE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) S[kb][gq] = floatx16{};
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8 ka = *(const bf16x8*)(Ks + kb * 32 * C::RBK + koff + ds * 32);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+          S[kb][gq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[gq][ds], S[kb][gq], 0, 0, 0);
+      }
+    }
+  };
+
+  // Coordinate mask of the tile in stage st (boundary and ragged tiles only),
+  // branch-free.  Key kk of the tile (kk = 32 kb + 8 (i / 4) + 4 hh + i % 4
+  // for accumulator element i) is an anchor key iff kk < P - key0, which can
+  // hold only on the tile that reaches into the first P positions.
+  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) {
+    if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return;
+    const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
+    const int lim_n = N - key0;           // kk >= lim_n: past the last token
+    const int lane_kk = 4 * hh;
+    if constexpr (BITS) {
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const uint32_t word = kb * 32 < lim_n ? bits_row[gq][(key0 >> 5) + kb] : 0u;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = kb * 32 + 8 * (i / 4) + (i % 4) + lane_kk;
+            const bool keep = ((word >> (kk & 31)) & 1u) & (kk < lim_n);
+            S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
+          }
+        }
+    } else if (kind == SVATTN_SPATIAL) {
+      // kept non-anchor keys: key - mq_a in [0, mq_b)
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) {
+        const int base = key0 + lane_kk - mq_a[gq];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = kb * 32 + 8 * (i / 4) + (i % 4);
+            const bool keep = ((uint32_t)(base + kk) < (uint32_t)mq_b[gq]) | (kk + lane_kk < lim_anchor);
+            S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
+          }
+      }
+    } else if (kind == SVATTN_TEMPORAL) {
+      const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
+      const bool any_anchor = lim_anchor > 0;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int kk0 = kb * 32 + 8 * i4 + lane_kk;
+          const int4 kc4 = *(const int4*)&kcs[st][kk0];
+          const int kcv[4] = {kc4.x, kc4.y, kc4.z, kc4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int yk = kcv[j] >> 16, xk = kcv[j] & 0xffff;
+            const bool anchor = any_anchor & (kk0 + j < lim_anchor);
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq) {
+              const bool keep = (((uint32_t)(yk - mq_a[gq]) + r <= r2) & ((uint32_t)(xk - mq_b[gq]) + r <= r2)) | anchor;
+              S[kb][gq][i4 * 4 + j] = keep ? S[kb][gq][i4 * 4 + j] : -INFINITY;
+            }
+          }
+        }
+      }
+    } else {  // dense: only the key range
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool keep = kb * 32 + 8 * (i / 4) + (i % 4) + lane_kk < lim_n;
+#pragma unroll
+          for (int gq = 0; gq < QG; ++gq) S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
+        }
+    }
+  };
+
+  // Online softmax of one tile's scores; P (bf16) is the B operand of P V.
+  auto softmax = [&](floatx16 (&S)[C::KB][QG], bf16x8 (&P)[2 * C::KB][QG]) {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][gq][i]);
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run[gq], mx);
+      const bool need = (m_new - m_run[gq]) * c > kRescaleThreshold;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_run[gq] - m_new) * c) : 1.0f;
+        if (need) m_run[gq] = m_new;
+        l_run[gq] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[gq][db] *= alpha;
+      }
+      const float mc = m_run[gq] * c;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 p;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][gq][h * 8 + j], c, -mc));
+            ls += e;
+            p[j] = (__bf16)e;
+          }
+          P[kb * 2 + h][gq] = p;
+        }
+      }
+      l_run[gq] += ls;
+    }
+  };
+
+  // O^T += V^T P^T for the tile in stage st.
+  auto pv = [&](int st, const bf16x8 (&P)[2 * C::KB][QG]) {
+    const char* Vs = smem + st * C::STAGE_BYTES + C::K_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 2 * C::KB; ++ks) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const char* base = Vs + ks * 16 * C::RBV + voff[db];
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(base));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(base + 8 * C::RBV));
+        const short4v both[2] = {lo, hi};
+        bf16x8 va;
+        __builtin_memcpy(&va, both, sizeof(va));
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+          acc[gq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[ks][gq], acc[gq][db], 0, 0, 0);
+      }
+    }
+  };
+
+  floatx16 SA[C::KB][QG], SB[C::KB][QG];
+  bf16x8 P[2 * C::KB][QG];
+
+  if constexpr (STAGES == 3) {
+    // Prologue: tiles 0 and 1 in flight, S of tile 0.
+    int key_next = n > 0 ? tile_key0(0) : 0;  // key0 of tile j+1 during step j
+    if (n > 0) issue(key_next, 0);
+    if (n > 1) issue(tile_key0(1), 1);
+    wait_tiles();
+    __syncthreads();
+    if (n > 0) {
+      qk(0, SA);
+      mask(0, key_next, tile_class(0), SA);
+    }
+    // One pipelined step: S of tile j+1 (MFMA) beside the softmax of tile j
+    // (VALU), then P V of tile j; tile j+2 streams into LDS meanwhile.
+    auto step = [&](int j, int st, floatx16 (&Scur)[C::KB][QG], floatx16 (&Snext)[C::KB][QG]) {
+      const int st1 = st == STAGES - 1 ? 0 : st + 1;
+      const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
+      if (j + 2 < n) issue(tile_key0(j + 2), st2);
+      int key1 = 0, cls1 = 0;
+      if (j + 1 < n) {
+        key1 = tile_key0(j + 1);
+        cls1 = tile_class(j + 1);
+        qk(st1, Snext);
+      }
+      softmax(Scur, P);
+      pv(st, P);
+      if (j + 1 < n) mask(st1, key1, cls1, Snext);
+      wait_tiles();
+      __syncthreads();
+    };
+    int st = 0;
+    for (int j = 0; j < n; j += 2) {
+      step(j, st, SA, SB);
+      st = st == STAGES - 1 ? 0 : st + 1;
+      if (j + 1 < n) {
+        step(j + 1, st, SB, SA);
+        st = st == STAGES - 1 ? 0 : st + 1;
+      }
+    }
+  } else {
+    if (n > 0) issue(tile_key0(0), 0);
+    wait_tiles();
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      const int st = j & 1;
+      if (j + 1 < n) issue(tile_key0(j + 1), st ^ 1);
+      qk(st, SA);
+      mask(st, tile_key0(j), tile_class(j), SA);
+      softmax(SA, P);
+      pv(st, P);
+      wait_tiles();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: O = acc / l, lse = m*scale + ln l ----
+  __bf16* __restrict__ O = (__bf16*)hd.o;
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    const int qi = q0 + gq * 32 + l32;
+    const float l = sum_xor32(l_run[gq]);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    if (qi < N) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = db * 32 + 8 * i4 + 4 * hh;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 ov;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc[gq][db][i4 * 4 + j] * inv);
+          *(bf16x4*)(O + (size_t)qi * D + d0) = ov;
+        }
+      }
+      if (hd.lse && hh == 0) hd.lse[qi] = l > 0.f ? m_run[gq] * hd.scale + __logf(l) : -INFINITY;
+    }
+  }
+}
+
+template <int D, int BK, int NW, int QG, int STAGES, bool BITS = false>
+hipError_t launch(const FwdArgs& a, hipStream_t st) {
+  const int per_round = 8 * a.chunk;
+  const int grid = ((a.n_items + per_round - 1) / per_round) * per_round;
+  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, STAGES, BITS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fwd2
+}  // namespace svattn

@@ -150,7 +150,9 @@ SVATTN_API int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t 
  *          of head h are in masks[h].order
  *   maps   host array [heads] of pointers to maps built for (geom, masks[h]);
  *          heads may share a map; all maps share one (block_q, block_k) with
- *          block_q in {32, 64, 128, 256} and block_k in {32, 64}
+ *          block_q in {32, 64, 128, 256} and block_k in {32, 64}; row_ptr,
+ *          col and col_cls must be 4-byte aligned (col_cls is read as aligned
+ *          4-byte words, never past byte n_qt * n_kt - 1)
  *   scales host array [heads], finite fp32 softmax scales > 0
  *   lse    optional device fp32 [heads, N]: natural-log sum of exp of kept
  *          scaled scores (NULL to skip)
