@@ -34,12 +34,12 @@
 // swizzled by the row (vswz): a transpose read covers rows 4a..4a+3, and the
 // swizzle gives each of those rows its own banks.
 //
-// Pipelining (STAGES == 3).  Iteration j computes S of tile j+1 on the MFMA
-// pipe while the VALU runs the softmax of tile j, then P V of tile j; the
-// loads of tile j+2 are in flight meanwhile.  A single barrier per iteration
-// suffices: the stage written at the end of iteration j held tile j-1, whose
-// last reader (P V of iteration j-1) finished before that barrier.
-// STAGES == 2 is the plain double-buffered loop.
+// Schedules.  The plain schedule (PP = false) runs every wave through
+// S, mask, softmax and P V of a tile, then one barrier; K/V of the next tile
+// stream into the other half of a double buffer meanwhile.  The two-group
+// schedule (PP = true, 8 waves) offsets waves 4-7 by half a tile so that on
+// each SIMD one wave's MFMA work overlaps the other wave's softmax; it keeps a
+// ring of three K/V stages (see the loop).
 //
 // Softmax.  exp2 with the scale folded into one FMA; masked scores are -inf.
 // The running max only moves when a new score exceeds it by more than 8 in
@@ -47,6 +47,8 @@
 // only by rounding.  P is rounded to bf16 for the P V product; the row sum
 // (and so lse) accumulates the fp32 values.
 #pragma once
+
+#include <type_traits>
 
 #include "internal.hpp"
 
@@ -59,7 +61,7 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
-template <int D, int BK, int NW, int QG, int STAGES>
+template <int D, int BK, int NW, int QG>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int BQ = NW * QG * 32;
@@ -74,6 +76,17 @@ struct Cfg {
   static constexpr int DS = D / 16;                       // 16-dim MFMA steps of Q K^T
   static constexpr int DB = D / 32;                       // 32-dim blocks of O
 };
+
+// Fragments of K (KPF) and of V (VPF) read from LDS ahead of the MFMA that
+// consumes them.
+#ifndef SVATTN_KPF
+#define SVATTN_KPF 4
+#endif
+#ifndef SVATTN_VPF
+#define SVATTN_VPF 3
+#endif
+constexpr int KPF = SVATTN_KPF;
+constexpr int VPF = SVATTN_VPF;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
@@ -116,11 +129,12 @@ __device__ __forceinline__ int key_coord(const Geo& g, int order, int key) {
   return (y << 16) | (p - y * g.W);
 }
 
-template <int D, int BK, int NW, int QG, int STAGES, bool BITS>
+template <int D, int BK, int NW, int QG, bool PP, bool BITS>
 __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
-  using C = Cfg<D, BK, NW, QG, STAGES>;
+  using C = Cfg<D, BK, NW, QG>;
   static_assert(BK % 32 == 0 && (D == 64 || D == 128), "tile shape");
-  static_assert(STAGES == 2 || STAGES == 3, "stages");
+  static_assert(!PP || NW == 8, "the two-group schedule pairs waves w and w + 4 on one SIMD");
+  constexpr int STAGES = PP ? 3 : 2;
   __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
 
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   const uint8_t* __restrict__ col_cls = hd.col_cls;
   const int32_t* __restrict__ col = hd.col + e0;
   // First key of list entry j.
-  auto tile_key0 = [&](int j) -> int {
+  auto tile_key0 = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (BITS) return j * BK;
     else return ld_const(col + j) * BK;
   };
@@ -226,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   // Class of list entry e0 + j, read with a scalar load of its aligned
   // 4-byte word (col_cls is 4-byte aligned); a byte read serves the last
   // partial word of the buffer.
-  auto tile_class = [&](int j) -> int {
+  auto tile_class = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (BITS) return SVATTN_TILE_BOUNDARY;
     const int e = e0 + j;
     if ((e | 3) < cap) {
@@ -236,40 +250,78 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     return __builtin_amdgcn_readfirstlane((int)col_cls[e]);
   };
 
-  // Issue the HBM -> LDS copies of K and V tile `key0` into stage st, and the
-  // key coordinates of temporal heads.  Wave w copies the 1 KB pieces
-  // w, w + NW, ... of the stage; lane L of a piece fills byte 16 L of it, i.e.
-  // one 16-byte chunk slot of a padded row, and fetches that chunk of the
-  // key's row (padding slots fetch the tile's first chunk).  The copies are
-  // issued as inline asm so that the compiler inserts no wait for them before
-  // the LDS reads of other stages; wait_tiles() waits for them.
-  auto issue = [&](int key0, int st) {
-    const uint32_t stage_lds = lds_base + st * C::STAGE_BYTES;
-    constexpr int OPS = C::K_PIECES + C::V_PIECES;
-    const int first = min(key0, N - 1) * D;
-#pragma unroll
-    for (int i = 0; i < (OPS + NW - 1) / NW; ++i) {
-      const int o = wave_u + i * NW;
-      if (OPS % NW != 0 && o >= OPS) break;
-      const bool is_k = o < C::K_PIECES;
-      const int byte = (is_k ? o : o - C::K_PIECES) * 1024 + lane * 16;
-      const int rb = is_k ? C::RBK : C::RBV;
-      const int row = byte / rb, slot = (byte - row * rb) >> 4;
-      const int chunk = is_k ? slot : (slot ^ vswz<D>(row));
-      const int off = (row < BK && slot < C::CPR) ? min(key0 + row, N - 1) * D + chunk * 8  // rows past N are masked
-                                                  : first;
-      const __bf16* src = (is_k ? K : V) + off;
-      const uint32_t dst = stage_lds + o * 1024;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+  // First key and class of list entry t (zeros past the end of the list).
+  auto fetch = [&](int t, int& key0, int& cls) __attribute__((always_inline)) {
+    if (t < n) {
+      key0 = tile_key0(t);
+      cls = tile_class(t);
     }
-    if (need_kc && tid < BK) kcs[st][tid] = fwd2::key_coord(g, order, key0 + tid);
+  };
+
+  // HBM -> LDS copies of K and V tiles.  A stage is OPS 1 KB pieces; lane L
+  // of a piece fills byte 16 L of it, i.e. one 16-byte chunk slot of a row,
+  // and fetches that chunk of the key's row (K padding slots fetch the tile's
+  // first chunk).  Copier wave c owns pieces c, c + NCW, ....  A copy
+  // blocks its wave until the vector-memory queue takes it, so the copies go
+  // where a wave has no LDS reads in flight and, in the two-group schedule,
+  // trickle through the softmax of the group without MFMA work.  They are
+  // inline asm, so the compiler adds no wait for them before the LDS reads of
+  // other stages; explicit waits precede the barriers.
+  constexpr int OPS = C::K_PIECES + C::V_PIECES;
+  constexpr int NCW = PP ? NW / 2 : NW;       // copier waves: group B, or all
+  constexpr int OPC = (OPS + NCW - 1) / NCW;  // pieces per copier wave
+  const int cw = PP ? wave_u - NW / 2 : wave_u;  // index among the copiers
+  // Byte offset, from the tile's first row, of the chunk each of this lane's
+  // pieces fetches.  A copy then needs no vector arithmetic: the tile's first
+  // row is a scalar base and the lane offset is precomputed (the rows past N
+  // of a ragged tile are clamped at issue instead).
+  int dma_off[OPC];
+#pragma unroll
+  for (int i = 0; i < OPC; ++i) {
+    const int o = cw + i * NCW;
+    const bool is_k = o < C::K_PIECES;
+    const int byte = (is_k ? o : o - C::K_PIECES) * 1024 + lane * 16;
+    const int rb = is_k ? C::RBK : C::RBV;
+    const int row = byte / rb, slot = (byte - row * rb) >> 4;
+    const bool real = row < BK && slot < C::CPR;
+    dma_off[i] = real ? (row * D + (is_k ? slot : (slot ^ vswz<D>(row))) * 8) * 2 : 0;
+  }
+  // Piece i of this wave for the tile starting at key0, into stage st.
+  auto issue_op = [&](int i, int key0, int st) __attribute__((always_inline)) {
+    const int o = cw + i * NCW;
+    if (cw < 0 || (OPS % NCW != 0 && o >= OPS)) return;
+    const bool is_k = o < C::K_PIECES;
+    // The tile's first row as a scalar base address (uniform by construction;
+    // readfirstlane makes that explicit for the asm's SGPR operand).
+    const uint64_t b64 = (uint64_t)((const char*)(is_k ? K : V) + (size_t)key0 * (D * 2));
+    const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b64 >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+    uint32_t off = (uint32_t)dma_off[i];
+    if (key0 + BK > N) {  // ragged tile: rows past N read row N-1 (their keys are masked)
+      const int row = (int)(off / (D * 2));
+      off = (uint32_t)((min(key0 + row, N - 1) - key0) * (D * 2) + (off - row * (D * 2)));
+    }
+    const uint32_t dst = lds_base + st * C::STAGE_BYTES + o * 1024;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(base) : "m0");
+  };
+  // Key coordinates of temporal heads for the tile starting at key0 (the
+  // first BK threads of the copier waves).
+  auto issue_kc = [&](int key0, int st) __attribute__((always_inline)) {
+    const int t = tid - (PP ? NW / 2 : 0) * 64;
+    if (need_kc && t >= 0 && t < BK) kcs[st][t] = fwd2::key_coord(g, order, key0 + t);
+  };
+  // All copies of a tile at once (prologue).
+  auto issue = [&](int key0, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < OPC; ++i) issue_op(i, key0, st);
+    issue_kc(key0, st);
   };
   // All of this wave's copies have landed in LDS (the barrier that follows
   // makes every wave's copies visible).
-  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto wait_tiles = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // S^T = K Q^T for the tile in stage st.
-  auto qk = [&](int st, floatx16 (&S)[C::KB][QG]) {
+  auto qk = [&](int st, floatx16 (&S)[C::KB][QG], auto&& after_mfma) __attribute__((always_inline)) {
     const char* Ks = smem + st * C::STAGE_BYTES;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -283,15 +335,26 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq)
           S[kb][gq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[gq][ds], S[kb][gq], 0, 0, 0);
+        after_mfma(ds * C::KB + kb);
       }
     }
+    // Interleave: KPF fragments ahead, then one MFMA group per fragment, so
+    // only a few K fragments are in registers at a time.
+    constexpr int NR = C::DS * C::KB;
+    __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+    for (int i = 0; i < NR - KPF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KPF * QG, 0);
   };
 
   // Coordinate mask of the tile in stage st (boundary and ragged tiles only),
   // branch-free.  Key kk of the tile (kk = 32 kb + 8 (i / 4) + 4 hh + i % 4
   // for accumulator element i) is an anchor key iff kk < P - key0, which can
   // hold only on the tile that reaches into the first P positions.
-  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) {
+  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
     if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return;
     const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
     const int lim_n = N - key0;           // kk >= lim_n: past the last token
@@ -358,7 +421,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   };
 
   // Online softmax of one tile's scores; P (bf16) is the B operand of P V.
-  auto softmax = [&](floatx16 (&S)[C::KB][QG], bf16x8 (&P)[2 * C::KB][QG]) {
+  auto softmax = [&](floatx16 (&S)[C::KB][QG], bf16x8 (&P)[2 * C::KB][QG], auto&& after_chunk) __attribute__((always_inline)) {
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
       float mx = -INFINITY;
@@ -390,6 +453,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
             p[j] = (__bf16)e;
           }
           P[kb * 2 + h][gq] = p;
+          after_chunk((gq * C::KB + kb) * 2 + h);
         }
       }
       l_run[gq] += ls;
@@ -397,7 +461,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   };
 
   // O^T += V^T P^T for the tile in stage st.
-  auto pv = [&](int st, const bf16x8 (&P)[2 * C::KB][QG]) {
+  auto pv = [&](int st, const bf16x8 (&P)[2 * C::KB][QG], auto&& after_mfma) __attribute__((always_inline)) {
     const char* Vs = smem + st * C::STAGE_BYTES + C::K_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 2 * C::KB; ++ks) {
@@ -412,64 +476,121 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq)
           acc[gq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[ks][gq], acc[gq][db], 0, 0, 0);
+        after_mfma(ks * C::DB + db);
       }
     }
+    // Interleave the transpose reads (two per fragment) with the MFMAs,
+    // VPF fragments ahead.
+    constexpr int NR = 2 * C::KB * C::DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+    for (int i = 0; i < NR - VPF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, VPF * QG, 0);
   };
 
-  floatx16 SA[C::KB][QG], SB[C::KB][QG];
+  floatx16 S[C::KB][QG];
   bf16x8 P[2 * C::KB][QG];
 
-  if constexpr (STAGES == 3) {
-    // Prologue: tiles 0 and 1 in flight, S of tile 0.
-    int key_next = n > 0 ? tile_key0(0) : 0;  // key0 of tile j+1 during step j
-    if (n > 0) issue(key_next, 0);
-    if (n > 1) issue(tile_key0(1), 1);
+  constexpr int NCH = 2 * C::KB * QG;  // softmax chunks per tile
+  // The copier's pieces spread over the softmax chunks of one tile.
+  auto dma_in_softmax = [&](int chunk, bool dma, int key0, int st) __attribute__((always_inline)) {
+    if (!dma) return;
+#pragma unroll
+    for (int i = 0; i < OPC; ++i)
+      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st);
+  };
+  auto next_stage = [&](int st) __attribute__((always_inline)) { return st == STAGES - 1 ? 0 : st + 1; };
+
+  int key_c = 0, cls_c = 0, key_n = 0, cls_n = 0;
+  fetch(0, key_c, cls_c);
+  fetch(1, key_n, cls_n);
+
+  if constexpr (PP) {
+    // Two wave groups, A = waves 0-3 and B = waves 4-7; waves w and w + 4
+    // share a SIMD.  Step j has two barrier-separated phases.  Group A runs
+    // its MFMA work (P V of tile j-1, then S = K Q^T of tile j) in the first
+    // phase and its VALU work (mask and softmax of tile j) in the second;
+    // group B runs the softmax of tile j-1 in the first phase and P V of tile
+    // j-1 plus S of tile j in the second.  So in every phase one wave of each
+    // SIMD feeds the matrix cores while the other runs the exponentials.
+    // Tile t lives in LDS stage t % 3: K of tile j is read during step j, V of
+    // tile j during step j+1, and group B copies tile j+1 during its softmax
+    // in step j into the stage of tile j-2, whose last reader finished in step
+    // j-1.  Each group has its own loop (a compile-time flag) so that the
+    // compiler sees which of S and P is live.
+    if (n > 0) issue(key_c, 0);
+    if (n > 1) issue(key_n, 1);
     wait_tiles();
     __syncthreads();
-    if (n > 0) {
-      qk(0, SA);
-      mask(0, key_next, tile_class(0), SA);
-    }
-    // One pipelined step: S of tile j+1 (MFMA) beside the softmax of tile j
-    // (VALU), then P V of tile j; tile j+2 streams into LDS meanwhile.
-    auto step = [&](int j, int st, floatx16 (&Scur)[C::KB][QG], floatx16 (&Snext)[C::KB][QG]) {
-      const int st1 = st == STAGES - 1 ? 0 : st + 1;
-      const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
-      if (j + 2 < n) issue(tile_key0(j + 2), st2);
-      int key1 = 0, cls1 = 0;
-      if (j + 1 < n) {
-        key1 = tile_key0(j + 1);
-        cls1 = tile_class(j + 1);
-        qk(st1, Snext);
-      }
-      softmax(Scur, P);
-      pv(st, P);
-      if (j + 1 < n) mask(st1, key1, cls1, Snext);
-      wait_tiles();
-      __syncthreads();
+    const bool grp_b = wave_u >= 4;
+    auto mfma_work = [&](int j, int sj, int sp) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      if (j >= 1) pv(sp, P, [](int) {});
+      if (j < n) qk(sj, S, [](int) {});
+      __builtin_amdgcn_s_setprio(0);
     };
-    int st = 0;
-    for (int j = 0; j < n; j += 2) {
-      step(j, st, SA, SB);
-      st = st == STAGES - 1 ? 0 : st + 1;
-      if (j + 1 < n) {
-        step(j + 1, st, SB, SA);
-        st = st == STAGES - 1 ? 0 : st + 1;
+    // key_c / cls_c: tile j; key_n / cls_n: tile j+1; key_p / cls_p: tile j-1
+    auto run = [&](auto group_b) __attribute__((always_inline)) {
+      constexpr bool B = decltype(group_b)::value;
+      int sj = 0;  // stage of tile j
+      int key_p = 0, cls_p = 0;
+      for (int j = 0; j <= n; ++j) {
+        const int sp = sj == 0 ? STAGES - 1 : sj - 1, sn = next_stage(sj);
+        int key_nn = 0, cls_nn = 0;
+        fetch(j + 2, key_nn, cls_nn);
+        if constexpr (!B) {
+          mfma_work(j, sj, sp);
+          __syncthreads();
+          if (j < n) {
+            mask(sj, key_c, cls_c, S);
+            softmax(S, P, [](int) {});
+          }
+        } else {
+          if (j >= 1) {
+            const bool dma = j + 1 < n;
+            if (dma) issue_kc(key_n, sn);
+            mask(sp, key_p, cls_p, S);
+            softmax(S, P, [&](int ch) { dma_in_softmax(ch, dma, key_n, sn); });
+          }
+          __syncthreads();
+          mfma_work(j, sj, sp);
+        }
+        wait_tiles();
+        __syncthreads();
+        key_p = key_c; cls_p = cls_c;
+        key_c = key_n; cls_c = cls_n;
+        key_n = key_nn; cls_n = cls_nn;
+        sj = sn;
       }
-    }
+    };
+    if (grp_b) run(std::true_type{});
+    else run(std::false_type{});
   } else {
-    if (n > 0) issue(tile_key0(0), 0);
+    // Every wave: S, mask and softmax of tile j, then the copies of tile j+1
+    // (into the stage of tile j-1; the wave has no LDS reads in flight here),
+    // then P V of tile j and one barrier.
+    if (n > 0) issue(key_c, 0);
     wait_tiles();
     __syncthreads();
+    int st = 0;  // stage of tile j
     for (int j = 0; j < n; ++j) {
-      const int st = j & 1;
-      if (j + 1 < n) issue(tile_key0(j + 1), st ^ 1);
-      qk(st, SA);
-      mask(st, tile_key0(j), tile_class(j), SA);
-      softmax(SA, P);
-      pv(st, P);
+      int key_nn = 0, cls_nn = 0;
+      fetch(j + 2, key_nn, cls_nn);
+      qk(st, S, [](int) {});
+      mask(st, key_c, cls_c, S);
+      softmax(S, P, [](int) {});
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < n) issue(key_n, next_stage(st));
+      __builtin_amdgcn_sched_barrier(0);
+      pv(st, P, [](int) {});
       wait_tiles();
       __syncthreads();
+      key_c = key_n; cls_c = cls_n;
+      key_n = key_nn; cls_n = cls_nn;
+      st = next_stage(st);
     }
   }
 
@@ -498,11 +619,11 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   }
 }
 
-template <int D, int BK, int NW, int QG, int STAGES, bool BITS = false>
+template <int D, int BK, int NW, int QG, bool PP, bool BITS = false>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
   const int per_round = 8 * a.chunk;
   const int grid = ((a.n_items + per_round - 1) / per_round) * per_round;
-  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, STAGES, BITS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 

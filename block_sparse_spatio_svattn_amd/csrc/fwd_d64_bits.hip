@@ -6,7 +6,7 @@ namespace svattn {
 
 hipError_t launch_forward_d64_bits(const FwdArgs& a, int block_q, int block_k, hipStream_t st) {
 #define SVATTN_CASE(BQ, BK) \
-  if (block_q == BQ && block_k == BK) return fwd2::launch<64, BK, BQ / 32, 1, 2, true>(a, st);
+  if (block_q == BQ && block_k == BK) return fwd2::launch<64, BK, BQ / 32, 1, false, true>(a, st);
   SVATTN_CASE(32, 32)
   SVATTN_CASE(32, 64)
   SVATTN_CASE(64, 32)

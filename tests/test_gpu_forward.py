@@ -217,3 +217,24 @@ def test_dense_mask_entry_matches_coordinate_masks(sv):
     for h in range(2):
         assert_close(f64_of(o[h]), ref[h][0], f"bits h{h}")
         assert (bits_of(o[h]) == bits_of(o2[h])).all()
+
+
+@pytest.mark.parametrize("geom,d,bk", [((5, 24, 40), 128, 64), ((3, 5, 7), 128, 64), ((2, 9, 11), 64, 32),
+                                       ((4, 8, 8), 128, 32)])
+def test_two_group_schedule_matches_plain_schedule(sv, geom, d, bk):
+    """A launch whose heads are all dense runs the two-group schedule (block_q
+    256); the same dense head next to a spatial head runs the plain schedule.
+    Both do the same arithmetic in the same order, so the dense head's output is
+    bit-identical, and it matches the oracle.  Covers ragged q- and k-tiles."""
+    F, H, W = geom
+    heads_pp = [synth.Head("dense"), synth.Head("dense")]
+    heads_plain = [synth.Head("dense"), synth.Head("spatial", window=0)]
+    wl = synth.Workload(name="sched", seed=91, frames=F, height=H, width=W, head_dim=d,
+                        heads=tuple(heads_pp), tiles=((256, bk),))
+    inp = synth.make_inputs(wl)
+    o_pp = _run_layer(sv, wl, inp, 256, bk)
+    o_plain = _run_layer(sv, wl.with_heads(heads_plain), inp, 256, bk)
+    assert (bits_of(o_pp[0]) == bits_of(o_plain[0])).all()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * 2)
+    for h in range(2):
+        assert_close(f64_of(o_pp[h]), ref[h][0], f"two-group dense h{h} {geom}")
