@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR",
-    "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY",
+    "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "FORWARD_WORKSPACE_BYTES",
+    "new_workspace",
     "SvattnError", "Geom", "Mask", "TileMap", "lib", "version",
     "tile_map_dims", "build_tile_map", "permutation_index", "permute_tokens",
     "unpermute", "forward", "forward_ptrs", "forward_dense_mask",
@@ -31,6 +32,7 @@ SPATIAL, TEMPORAL, DENSE = 0, 1, 2
 FRAME_MAJOR, TEMPORAL_MAJOR = 0, 1
 TILE_EMPTY, TILE_BOUNDARY, TILE_FULL = 0, 1, 2
 MAP_ALL_BOUNDARY = 1
+FORWARD_WORKSPACE_BYTES = 256  # SVATTN_FORWARD_WORKSPACE_BYTES
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvattn.so")
 
@@ -66,7 +68,7 @@ class Mask(ctypes.Structure):
 
 class _TileMapC(ctypes.Structure):
     _fields_ = [("block_q", _i32), ("block_k", _i32), ("n_qt", _i32), ("n_kt", _i32),
-                ("cls", _vp), ("row_ptr", _vp), ("col", _vp), ("col_cls", _vp)]
+                ("cls", _vp), ("row_ptr", _vp), ("col", _vp), ("col_cls", _vp), ("qt_order", _vp)]
 
 
 _LIB = None
@@ -93,9 +95,9 @@ def lib() -> ctypes.CDLL:
     L.svattn_permute_tokens.argtypes = [P(Geom), _i32, _i32, _vp, _vp, _vp]
     L.svattn_unpermute.argtypes = [P(Geom), _i32, _i32, _vp, _vp, _vp]
     L.svattn_forward.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
-                                 _vp, _vp, _vp, _vp, _vp, _vp]
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.svattn_forward_ptrs.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
-                                      P(_vp), P(_vp), P(_vp), P(_vp), P(_vp), _vp]
+                                      P(_vp), P(_vp), P(_vp), P(_vp), P(_vp), _vp, _vp]
     L.svattn_forward_dense_mask.argtypes = [_i32, _i32, _i32, _vp, _i32, P(ctypes.c_float),
                                             _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     for f in ("svattn_tile_map_dims", "svattn_build_tile_map", "svattn_build_tile_map_ex",
@@ -140,7 +142,8 @@ def tile_map_dims(geom: Geom, block_q: int, block_k: int):
 
 
 class TileMap:
-    """Device buffers of one tile map (classes + CSR list of non-empty k-tiles)."""
+    """Device buffers of one tile map (classes, CSR list of non-empty k-tiles and
+    the longest-row-first q-tile order)."""
 
     def __init__(self, geom: Geom, block_q: int, block_k: int, device="cuda"):
         self.geom = geom
@@ -151,9 +154,11 @@ class TileMap:
         self.row_ptr = torch.empty(self.n_qt + 1, dtype=torch.int32, device=device)
         self.col = torch.empty(cap, dtype=torch.int32, device=device)
         self.col_cls = torch.empty(cap, dtype=torch.uint8, device=device)
+        self.qt_order = torch.empty(self.n_qt, dtype=torch.int32, device=device)
         self.c = _TileMapC(block_q, block_k, self.n_qt, self.n_kt,
                            _dev(self.cls, "cls"), _dev(self.row_ptr, "row_ptr"),
-                           _dev(self.col, "col"), _dev(self.col_cls, "col_cls"))
+                           _dev(self.col, "col"), _dev(self.col_cls, "col_cls"),
+                           _dev(self.qt_order, "qt_order"))
 
     def rebuild(self, mask: Mask, flags: int = 0, stream=None) -> "TileMap":
         """Run the tile classifier into this map's buffers (no allocation)."""
@@ -220,14 +225,28 @@ def _scales(scales, heads):
     return (ctypes.c_float * heads)(*s)
 
 
+def new_workspace(device="cuda") -> torch.Tensor:
+    """Device buffer for the persistent schedule of forward / forward_ptrs."""
+    return torch.empty(FORWARD_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None
+    if workspace.numel() * workspace.element_size() < FORWARD_WORKSPACE_BYTES:
+        raise SvattnError(f"workspace must hold at least {FORWARD_WORKSPACE_BYTES} bytes")
+    return _dev(workspace, "workspace")
+
+
 def forward(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             masks: Sequence[Mask], maps: Sequence[TileMap], scales: Sequence[float],
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            stream=None) -> torch.Tensor:
+            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Block-sparse attention forward over [heads, N, d] bf16 tensors.
 
     Head h's tensors are in masks[h].order; maps[h] must be built for
-    (geom, masks[h]).  ``lse`` (fp32 [heads, N]) is filled if given.
+    (geom, masks[h]).  ``lse`` (fp32 [heads, N]) is filled if given.  With a
+    ``workspace`` (new_workspace()) the persistent schedule runs.
     """
     heads = q.shape[0]
     out = _qkvo(q, k, v, out, geom.n)
@@ -240,14 +259,15 @@ def forward(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check(lib().svattn_forward(ctypes.byref(geom), heads, q.shape[2], marr, parr, _scales(scales, heads),
                                 _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
                                 _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
-                                lse_p, _stream(stream)), "svattn_forward")
+                                lse_p, _ws(workspace), _stream(stream)), "svattn_forward")
     return out
 
 
 def forward_ptrs(geom: Geom, qs: Sequence[torch.Tensor], ks: Sequence[torch.Tensor],
                  vs: Sequence[torch.Tensor], os_: Sequence[torch.Tensor], masks: Sequence[Mask],
                  maps: Sequence[TileMap], scales: Sequence[float],
-                 lses: Optional[Sequence[Optional[torch.Tensor]]] = None, stream=None) -> None:
+                 lses: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Forward with one [N, d] bf16 tensor per head (outputs written into ``os_``)."""
     heads = len(qs)
     if not (len(ks) == len(vs) == len(os_) == len(masks) == len(maps) == heads):
@@ -268,7 +288,7 @@ def forward_ptrs(geom: Geom, qs: Sequence[torch.Tensor], ks: Sequence[torch.Tens
     _check(lib().svattn_forward_ptrs(ctypes.byref(geom), heads, d, marr, parr, _scales(scales, heads),
                                      arr(qs, "q", torch.bfloat16), arr(ks, "k", torch.bfloat16),
                                      arr(vs, "v", torch.bfloat16), arr(os_, "o", torch.bfloat16),
-                                     lse_arr, _stream(stream)), "svattn_forward_ptrs")
+                                     lse_arr, _ws(workspace), _stream(stream)), "svattn_forward_ptrs")
 
 
 def forward_dense_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bits: torch.Tensor,

@@ -103,6 +103,12 @@ int check_map_buffers(const svattn_tile_map* map, const char* who) {
 // SIMD partner's softmax) wins when no tile needs a mask; with boundary tiles
 // the masked softmax phase becomes its long pole and the plain schedule wins
 // (measured at 75,600 tokens, 256 x 64 tiles).
+// Clears the work counter of the persistent schedule.  A kernel rather than a
+// memset, so that a captured graph replays it correctly.
+__global__ void clear_queue_kernel(uint32_t* q) {
+  if (threadIdx.x == 0) q[0] = 0u;
+}
+
 hipError_t dispatch_forward(const FwdArgs& a, int head_dim, int bq, int bk, hipStream_t st) {
   if (a.dense_bits)
     return head_dim == 128 ? launch_forward_d128_bits(a, bq, bk, st) : launch_forward_d64_bits(a, bq, bk, st);
@@ -161,8 +167,8 @@ int svattn_build_tile_map_ex(const svattn_geom* geom, const svattn_mask* mask, s
   if ((int64_t)map->n_qt * map->n_kt >= (1ll << 31))
     return fail(SVATTN_ERR_UNSUPPORTED, "tile map of %d x %d blocks is too large", map->n_qt, map->n_kt);
   if ((s = check_map_buffers(map, "svattn_build_tile_map"))) return s;
-  if (!aligned(map->row_ptr, 4) || !aligned(map->col, 4))
-    return fail(SVATTN_ERR_INVALID_ARG, "row_ptr / col must be 4-byte aligned");
+  if (!aligned(map->row_ptr, 4) || !aligned(map->col, 4) || !aligned(map->qt_order, 4))
+    return fail(SVATTN_ERR_INVALID_ARG, "row_ptr / col / qt_order must be 4-byte aligned");
   const Geo g = make_geo(*geom);
   hipError_t e = launch_tile_map(g, *mask, *map, flags, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tile map launch");
@@ -265,6 +271,20 @@ static int check_ptrs(const std::vector<HeadPtrs>& p, int64_t n, int32_t head_di
   return SVATTN_OK;
 }
 
+// The forward workspace: NULL, or SVATTN_FORWARD_WORKSPACE_BYTES of device
+// memory, 4-byte aligned, overlapping no tensor of the call.
+static int check_workspace(const std::vector<HeadPtrs>& p, int64_t n, int32_t head_dim, const void* ws) {
+  if (!ws) return SVATTN_OK;
+  if (!aligned(ws, 4)) return fail(SVATTN_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+  const size_t bytes = (size_t)n * head_dim * 2, lb = (size_t)n * 4, wb = SVATTN_FORWARD_WORKSPACE_BYTES;
+  for (size_t h = 0; h < p.size(); ++h) {
+    if (overlap(ws, wb, p[h].q, bytes) || overlap(ws, wb, p[h].k, bytes) || overlap(ws, wb, p[h].v, bytes) ||
+        overlap(ws, wb, p[h].o, bytes) || (p[h].lse && overlap(ws, wb, p[h].lse, lb)))
+      return fail(SVATTN_ERR_INVALID_ARG, "workspace overlaps a tensor of head %zu", h);
+  }
+  return SVATTN_OK;
+}
+
 static std::vector<HeadPtrs> contiguous_ptrs(int64_t n, int32_t heads, int32_t head_dim, const void* q,
                                              const void* k, const void* v, void* o, float* lse) {
   std::vector<HeadPtrs> p(heads);
@@ -287,6 +307,12 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
     for (int i = 0; i < nh; ++i) a.heads[i] = descs[h0 + i];
     a.n_slots = nh;
     a.n_items = nh * a.n_qt;
+    if (a.queue) {
+      // launches on one stream run in order, so one counter serves them all
+      hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, st, a.queue);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "work counter clear");
+    }
     hipError_t e = dispatch_forward(a, head_dim, bq, bk, st);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
   }
@@ -295,7 +321,7 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
 
 static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32_t head_dim,
                         const svattn_mask* masks, const svattn_tile_map* const* maps, const float* scales,
-                        const std::vector<HeadPtrs>& ptrs, void* stream) {
+                        const std::vector<HeadPtrs>& ptrs, void* workspace, void* stream) {
   int s;
   if (!masks || !maps) return fail(SVATTN_ERR_INVALID_ARG, "masks / maps is NULL");
   int bq = 0, bk = 0;
@@ -318,8 +344,11 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
     if (!m->row_ptr || !m->col || !m->col_cls) return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] buffer is NULL", h);
     if (!aligned(m->row_ptr, 4) || !aligned(m->col, 4) || !aligned(m->col_cls, 4))
       return fail(SVATTN_ERR_INVALID_ARG, "maps[%d]: row_ptr, col and col_cls must be 4-byte aligned", h);
+    if (m->qt_order && !aligned(m->qt_order, 4))
+      return fail(SVATTN_ERR_INVALID_ARG, "maps[%d]: qt_order must be 4-byte aligned", h);
   }
   if ((s = check_ptrs(ptrs, n, head_dim))) return s;
+  if ((s = check_workspace(ptrs, n, head_dim, workspace))) return s;
 
   std::vector<HeadDesc> descs(heads);
   std::vector<double> cost(heads);
@@ -335,6 +364,7 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
     d.row_ptr = maps[h]->row_ptr;
     d.col = maps[h]->col;
     d.col_cls = maps[h]->col_cls;
+    d.qt_order = maps[h]->qt_order;
     d.scale = scales[h];
     d.scale_log2 = scales[h] * kLog2eHost;
     d.kind = masks[h].kind;
@@ -356,25 +386,26 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
   a.n_kt = (int32_t)cdiv(n, bk);
   a.chunk = 32;
   a.dense_bits = 0;
+  a.queue = (uint32_t*)workspace;
   return run_launches(a, sorted, head_dim, bq, bk, (hipStream_t)stream);
 }
 
 int svattn_forward(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
                    const svattn_tile_map* const* maps, const float* scales, const void* q, const void* k,
-                   const void* v, void* o, float* lse, void* stream) {
+                   const void* v, void* o, float* lse, void* workspace, void* stream) {
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
   if ((s = check_common(heads, head_dim, scales))) return s;
   if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
   return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
-                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), stream);
+                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream);
 }
 
 int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
                         const svattn_tile_map* const* maps, const float* scales, const void* const* q,
                         const void* const* k, const void* const* v, void* const* o, float* const* lse,
-                        void* stream) {
+                        void* workspace, void* stream) {
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
@@ -382,7 +413,7 @@ int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim
   if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o pointer array is NULL");
   std::vector<HeadPtrs> p(heads);
   for (int h = 0; h < heads; ++h) p[h] = HeadPtrs{q[h], k[h], v[h], o[h], lse ? lse[h] : nullptr};
-  return forward_impl(geom, n, heads, head_dim, masks, maps, scales, p, stream);
+  return forward_impl(geom, n, heads, head_dim, masks, maps, scales, p, workspace, stream);
 }
 
 int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim, const uint32_t* mask_bits,

@@ -129,7 +129,7 @@ __device__ __forceinline__ int key_coord(const Geo& g, int order, int key) {
   return (y << 16) | (p - y * g.W);
 }
 
-template <int D, int BK, int NW, int QG, bool PP, bool BITS>
+template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST>
 __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   using C = Cfg<D, BK, NW, QG>;
   static_assert(BK % 32 == 0 && (D == 64 || D == 128), "tile shape");
@@ -138,18 +138,34 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
 
-  // ---- work item: XCD-aware order (workgroup b runs on XCD b % 8) ----
-  const int b = blockIdx.x;
-  const int xcd = b & 7, s = b >> 3;
-  const int item = ((s / a.chunk) * 8 + xcd) * a.chunk + (s % a.chunk);
-  if (item >= a.n_items) return;
+  __shared__ int ticket;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // ---- work items ----
+  // Static schedule (no queue): one item per workgroup, XCD-aware (workgroup
+  // b runs on XCD b % 8).  Persistent schedule: as many workgroups as fit on
+  // the chip at once, each taking the next item from a counter until the
+  // items run out.  A chip hands the workgroups of a grid to its shader
+  // engines in a fixed rotation, so with items of unequal length a static
+  // grid leaves compute units idle while work waits for another engine; a
+  // shared counter keeps every resident workgroup busy to the end.
+  int item;
+  if constexpr (!PST) {
+    const int b = blockIdx.x;
+    const int xcd = b & 7, s = b >> 3;
+    item = ((s / a.chunk) * 8 + xcd) * a.chunk + (s % a.chunk);
+  } else {
+    if (tid == 0) ticket = (int)atomicAdd(a.queue, 1u);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(ticket);
+  }
+  while (item < a.n_items) {
   const int slot = item / a.n_qt;
-  const int qt = item - slot * a.n_qt;
   const HeadDesc& hd = a.heads[slot];
+  const int qt = (BITS || !hd.qt_order) ? item - slot * a.n_qt : ld_const(hd.qt_order + (item - slot * a.n_qt));
   const Geo g = a.g;
   const int N = g.N;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int l32 = lane & 31, hh = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
@@ -617,13 +633,56 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
       if (hd.lse && hh == 0) hd.lse[qi] = l > 0.f ? m_run[gq] * hd.scale + __logf(l) : -INFINITY;
     }
   }
+
+  if constexpr (!PST) break;
+  __syncthreads();  // every wave has read the previous ticket
+  if (tid == 0) ticket = (int)atomicAdd(a.queue, 1u);
+  __syncthreads();
+  item = __builtin_amdgcn_readfirstlane(ticket);
+  }  // items
 }
 
+// Workgroups of this kernel resident on the current device at once (cached
+// per device).
+template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST>
+hipError_t resident_workgroups(int* out) {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd2_kernel<D, BK, NW, QG, PP, BITS, PST>, NW * 64, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    v = per_cu * cus > 0 ? per_cu * cus : 1;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  *out = v;
+  return hipSuccess;
+}
+
+// Persistent schedule when a queue is given (plain schedule over a tile map
+// only: the two-group schedule serves launches of equal-length rows, where a
+// static grid already balances), else the static grid.
 template <int D, int BK, int NW, int QG, bool PP, bool BITS = false>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
+  if constexpr (!PP && !BITS) {
+    if (a.queue) {
+      int resident = 0;
+      hipError_t e = resident_workgroups<D, BK, NW, QG, PP, BITS, true>(&resident);
+      if (e != hipSuccess) return e;
+      const int grid = resident < a.n_items ? resident : a.n_items;
+      hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS, true>), dim3(grid), dim3(NW * 64), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   const int per_round = 8 * a.chunk;
   const int grid = ((a.n_items + per_round - 1) / per_round) * per_round;
-  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS, false>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "svattn.h"
 
 namespace svattn {
@@ -93,6 +95,7 @@ struct HeadDesc {
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* col_cls;
+  const int32_t* qt_order;  // visiting order of q-tiles, or nullptr for index order
   const uint32_t* bits;  // dense-mask mode: [N][ceil(N/32)] words of this head
   float scale_log2;      // scale * log2(e)
   float scale;
@@ -100,6 +103,7 @@ struct HeadDesc {
 };
 
 constexpr int kMaxHeadsPerLaunch = 16;
+constexpr int kMaxDevices = 64;
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 struct FwdArgs {
@@ -107,7 +111,8 @@ struct FwdArgs {
   int32_t n_qt, n_kt;
   int32_t n_items;        // heads_in_launch * n_qt
   int32_t n_slots;        // heads in this launch
-  int32_t chunk;          // consecutive work items kept on one XCD
+  int32_t chunk;          // consecutive work items kept on one XCD (static schedule)
+  uint32_t* queue;        // zeroed work counter (persistent schedule), or nullptr
   int32_t dense_bits;     // 1: visit every k-tile and mask from bits
   int32_t words_per_row;  // ceil(N/32) for the bit mask
   HeadDesc heads[kMaxHeadsPerLaunch];

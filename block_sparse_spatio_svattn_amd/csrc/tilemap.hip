@@ -195,6 +195,29 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(svattn_tile_map map) 
   }
 }
 
+// Pass 4 (when qt_order is requested): rank of each q-tile under the order
+// (longer row first, then smaller index), a strict total order, so
+// qt_order[rank] = qt is a permutation.  One thread per q-tile compares its
+// row length with every other row's, read through LDS in chunks.
+__global__ __launch_bounds__(kThreads) void order_kernel(svattn_tile_map map) {
+  __shared__ int len[kThreads];
+  const int qt = blockIdx.x * kThreads + threadIdx.x;
+  const int mine = qt < map.n_qt ? map.row_ptr[qt + 1] - map.row_ptr[qt] : 0;
+  int rank = 0;
+  for (int j0 = 0; j0 < map.n_qt; j0 += kThreads) {
+    const int j = j0 + threadIdx.x;
+    len[threadIdx.x] = j < map.n_qt ? map.row_ptr[j + 1] - map.row_ptr[j] : -1;
+    __syncthreads();
+    const int lim = min(kThreads, map.n_qt - j0);
+    for (int i = 0; i < lim; ++i) {
+      const int l = len[i];
+      rank += (l > mine) | ((l == mine) & (j0 + i < qt));
+    }
+    __syncthreads();
+  }
+  if (qt < map.n_qt) map.qt_order[rank] = qt;
+}
+
 }  // namespace
 
 hipError_t launch_tile_map(const Geo& g, const svattn_mask& m, const svattn_tile_map& map, uint32_t flags,
@@ -206,6 +229,9 @@ hipError_t launch_tile_map(const Geo& g, const svattn_mask& m, const svattn_tile
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3(map.n_qt), dim3(kThreads), 0, st, map);
+  e = hipGetLastError();
+  if (e != hipSuccess || !map.qt_order) return e;
+  hipLaunchKernelGGL(order_kernel, dim3((map.n_qt + kThreads - 1) / kThreads), dim3(kThreads), 0, st, map);
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (FRAME_MAJOR, TEMPORAL_MAJOR, Geom, Mask, SvattnError, TileMap, build_tile_map,
+from . import (FRAME_MAJOR, TEMPORAL_MAJOR, Geom, Mask, SvattnError, TileMap, build_tile_map, new_workspace,
                forward_ptrs, permute_tokens, unpermute)
 
 
@@ -31,7 +31,7 @@ def _runs(idx: List[int]) -> List[Tuple[int, int]]:
 
 class SparseVideoAttention:
     def __init__(self, geom: Geom, masks: Sequence[Mask], head_dim: int, block_q: int = 256,
-                 block_k: int = 64, device="cuda", map_flags: int = 0):
+                 block_k: int = 64, device="cuda", map_flags: int = 0, persistent: bool = True):
         self.geom = geom
         self.masks = [Mask(m.kind, m.order, m.window, m.radius) for m in masks]
         self.head_dim = head_dim
@@ -48,6 +48,8 @@ class SparseVideoAttention:
         self.tm_runs = _runs(self.tm_heads)
         self._slot = {h: i for i, h in enumerate(self.tm_heads)}
         self._buf = None
+        # work counter of the persistent schedule (None: static grid)
+        self.workspace = new_workspace(device) if persistent else None
 
     def _buffers(self):
         if self._buf is None:
@@ -76,7 +78,8 @@ class SparseVideoAttention:
                 qs.append(qt[s]); ks.append(kt[s]); vs.append(vt[s]); os_.append(ot[s])
             else:
                 qs.append(q[h]); ks.append(k[h]); vs.append(v[h]); os_.append(out[h])
-        forward_ptrs(self.geom, qs, ks, vs, os_, self.masks, self.maps, scales, stream=stream)
+        forward_ptrs(self.geom, qs, ks, vs, os_, self.masks, self.maps, scales, workspace=self.workspace,
+                     stream=stream)
 
     def unpermute_output(self, out, stream=None):
         if not self.tm_heads:

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SVATTN_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define SVATTN_VERSION 10100 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 #define SVATTN_OK 0
@@ -67,6 +67,9 @@ extern "C" {
 #define SVATTN_TILE_EMPTY 0
 #define SVATTN_TILE_BOUNDARY 1
 #define SVATTN_TILE_FULL 2
+
+/* Size of the optional workspace of svattn_forward / svattn_forward_ptrs. */
+#define SVATTN_FORWARD_WORKSPACE_BYTES 256
 
 /* Flags for svattn_build_tile_map_ex. */
 #define SVATTN_MAP_ALL_BOUNDARY 1u  /* mark every non-empty tile BOUNDARY (the naive
@@ -92,6 +95,12 @@ typedef struct {
  *   row_ptr int32 [n_qt + 1]      row_ptr[0] = 0, nnz = row_ptr[n_qt]
  *   col     int32 [n_qt * n_kt]   capacity; entries [row_ptr[qt], row_ptr[qt+1])
  *   col_cls uint8 [n_qt * n_kt]   class of each listed block (BOUNDARY or FULL)
+ *   qt_order int32 [n_qt]         optional (NULL: not built, q-tiles run in index
+ *                                 order): the q-tile indices sorted by decreasing
+ *                                 row length row_ptr[qt+1] - row_ptr[qt], equal
+ *                                 lengths by increasing index.  The forward runs
+ *                                 long rows first so short rows fill the end of
+ *                                 the launch; results do not depend on it.
  * n_qt = ceil(N / block_q), n_kt = ceil(N / block_k) (svattn_tile_map_dims).
  */
 typedef struct {
@@ -100,6 +109,7 @@ typedef struct {
   int32_t* row_ptr;
   int32_t* col;
   uint8_t* col_cls;
+  int32_t* qt_order;
 } svattn_tile_map;
 
 /* Host only.  n_qt / n_kt for a geometry and tile shape.
@@ -110,7 +120,8 @@ SVATTN_API int svattn_tile_map_dims(const svattn_geom* geom, int32_t block_q, in
 /*
  * Tile classifier (the empty / full / boundary split of the aihirek.info page,
  * section "A TPU-kernel kialakítása döntőnek bizonyult", paragraphs 2-3).
- * Fills map->cls, row_ptr, col, col_cls for `mask` in `mask->order`.  Exact:
+ * Fills map->cls, row_ptr, col, col_cls (and qt_order if not NULL) for `mask`
+ * in `mask->order`.  Exact:
  * classes are derived from the token coordinates of each block, not sampled.
  * map->block_q/block_k/n_qt/n_kt must be set (n_qt/n_kt as from
  * svattn_tile_map_dims).  The map depends only on (geom, mask, tile shape) and
@@ -157,13 +168,23 @@ SVATTN_API int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t 
  *   lse    optional device fp32 [heads, N]: natural-log sum of exp of kept
  *          scaled scores (NULL to skip)
  * bf16 in, fp32 accumulation and softmax, bf16 out (round to nearest even).
+ *   workspace  NULL, or caller-owned device memory of at least
+ *          SVATTN_FORWARD_WORKSPACE_BYTES, 4-byte aligned, overlapping no
+ *          tensor of the call.  With it the forward runs a persistent
+ *          schedule: as many workgroups as the GPU holds at once take q-tiles
+ *          from a counter in the workspace, in the maps' qt_order (longest rows
+ *          first), so rows of unequal length keep every compute unit busy to
+ *          the end.  The library clears the counter on `stream` before each
+ *          launch; calls that can run at the same time (other streams) need
+ *          distinct workspaces.  Its contents after the call are unspecified.
  * head_dim in {64, 128}.  o (and lse) must not overlap q, k or v.  The result
- * does not depend on the order of heads or on which heads share a map.
+ * does not depend on the order of heads, on which heads share a map, on
+ * qt_order or on the workspace: the output is bit-identical either way.
  */
 SVATTN_API int svattn_forward(const svattn_geom* geom, int32_t heads, int32_t head_dim,
                               const svattn_mask* masks, const svattn_tile_map* const* maps,
                               const float* scales, const void* q, const void* k, const void* v,
-                              void* o, float* lse, void* stream);
+                              void* o, float* lse, void* workspace, void* stream);
 
 /*
  * Same as svattn_forward, with a separate device pointer per head instead of
@@ -177,7 +198,7 @@ SVATTN_API int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32
                                    const svattn_mask* masks, const svattn_tile_map* const* maps,
                                    const float* scales, const void* const* q, const void* const* k,
                                    const void* const* v, void* const* o, float* const* lse,
-                                   void* stream);
+                                   void* workspace, void* stream);
 
 /*
  * Reference forward for an arbitrary mask given as bits (for checking and

@@ -48,6 +48,7 @@ from .core import (  # noqa: F401
     kept_counts_per_row,
     tile_counts,
     tile_map,
+    qtile_order,
     attend_rows,
     attend_head,
     unpermute_rows,

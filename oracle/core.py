@@ -163,6 +163,18 @@ def tile_map(g: Geometry, kind: str, window: int, radius: int, order: str,
             np.asarray(col_cls, dtype=np.uint8))
 
 
+def qtile_order(row_ptr: np.ndarray) -> np.ndarray:
+    """Visiting order of the q-tiles of a tile map: indices sorted by decreasing
+    row length row_ptr[qt+1] - row_ptr[qt], equal lengths by increasing index.
+
+    The pages leave the order in which query tiles are processed open (each
+    q-tile's output is independent of the others); this order is the library's
+    longest-first schedule, stated here so the map can be checked exactly.
+    """
+    lengths = np.diff(np.asarray(row_ptr, dtype=np.int64))
+    return np.argsort(-lengths, kind="stable").astype(np.int32)
+
+
 # ---------------------------------------------------------------------------
 # Attention (aihirek page, SVG section paragraph 1: softmax attention over the
 # kept pairs).  O = softmax(S + M) V with S = Q K^T * scale, M = 0 or -inf.

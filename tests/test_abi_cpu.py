@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.version() == 10000
+    assert sv.version() == 10100
     L = sv.lib()
     for code, name in [(0, b"SVATTN_OK"), (1, b"SVATTN_ERR_INVALID_ARG"), (2, b"SVATTN_ERR_UNSUPPORTED"),
                        (3, b"SVATTN_ERR_HIP"), (99, b"SVATTN_ERR_UNKNOWN")]:
@@ -88,6 +88,7 @@ def test_build_tile_map_validation():
         (good_mask, _map(g, 64, 64, n_qt=3), 0, INVALID),                       # wrong dims
         (good_mask, _map(g, 64, 64, col=None), 0, INVALID),                     # NULL buffer
         (good_mask, _map(g, 64, 64, row_ptr=FAKE + 2), 0, INVALID),             # misaligned
+        (good_mask, _map(g, 64, 64, qt_order=FAKE + 2), 0, INVALID),            # misaligned order
         (good_mask, _map(g, 64, 64), 4, INVALID),                               # unknown flag
     ]
     for m, mp, flags, want in cases:
@@ -109,7 +110,7 @@ def test_permute_validation():
 
 
 def _fwd(L, g, heads=2, d=128, masks=None, maps=None, scales=None, q=FAKE, k=FAKE * 16, v=FAKE * 32,
-         o=FAKE * 64, lse=None):
+         o=FAKE * 64, lse=None, workspace=None):
     masks = masks or [sv.Mask(sv.SPATIAL, 0, 1, 0)] * heads
     maps = maps or [_map(g, 256, 64)] * heads
     scales = scales or [0.1] * heads
@@ -117,7 +118,7 @@ def _fwd(L, g, heads=2, d=128, masks=None, maps=None, scales=None, q=FAKE, k=FAK
     P = ctypes.POINTER(sv._TileMapC)
     parr = (P * heads)(*[ctypes.pointer(m) for m in maps])
     sarr = (ctypes.c_float * heads)(*scales)
-    return L.svattn_forward(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o, lse, None)
+    return L.svattn_forward(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o, lse, workspace, None)
 
 
 def test_forward_validation():
@@ -137,7 +138,12 @@ def test_forward_validation():
     assert _fwd(L, g, maps=[_map(g, 256, 64, n_kt=5)] * 2) == INVALID
     assert _fwd(L, g, maps=[_map(g, 256, 64, col_cls=None)] * 2) == INVALID
     assert _fwd(L, g, masks=[sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR, 1, 0)] * 2) == UNSUPPORTED
-    assert L.svattn_forward(ctypes.byref(g), 2, 128, None, None, None, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+    assert L.svattn_forward(ctypes.byref(g), 2, 128, None, None, None, FAKE, FAKE, FAKE, FAKE, None, None,
+                            None) == INVALID
+    assert _fwd(L, g, maps=[_map(g, 256, 64, qt_order=FAKE + 2)] * 2) == INVALID  # misaligned order
+    assert _fwd(L, g, workspace=FAKE * 128 + 2) == INVALID                    # misaligned workspace
+    assert _fwd(L, g, workspace=FAKE * 64 + 512) == INVALID                   # workspace inside o
+    assert "workspace" in _err()
 
 
 def test_forward_ptrs_and_dense_mask_validation():
@@ -154,12 +160,12 @@ def test_forward_ptrs_and_dense_mask_validation():
     q, k, v = VP(FAKE, FAKE + hb), VP(FAKE * 16, FAKE * 16 + hb), VP(FAKE * 32, FAKE * 32 + hb)
     o_overlap = VP(FAKE * 64, FAKE * 64 + 16)                # two heads' outputs overlap
     assert L.svattn_forward_ptrs(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o_overlap, None,
-                                 None) == INVALID
+                                 None, None) == INVALID
     o_in = VP(FAKE * 64, FAKE + hb)                           # head 1 writes over q of head 1
     assert L.svattn_forward_ptrs(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, o_in, None,
-                                 None) == INVALID
+                                 None, None) == INVALID
     assert L.svattn_forward_ptrs(ctypes.byref(g), heads, d, marr, parr, sarr, q, k, v, None, None,
-                                 None) == INVALID
+                                 None, None) == INVALID
     # dense-mask entry
     assert L.svattn_forward_dense_mask(2, 0, 64, FAKE, 1, sarr, FAKE, FAKE * 16, FAKE * 32, FAKE * 64, None,
                                        64, 32, None) == INVALID
@@ -183,3 +189,9 @@ def test_valid_call_without_device_reports_hip_error():
     st = L.svattn_permutation_index(ctypes.byref(g), FAKE, None, None)
     assert st == HIP
     assert len(_err()) > 0
+
+
+def test_workspace_size_matches_header():
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "svattn.h")).read()
+    m = re.search(r"#define SVATTN_FORWARD_WORKSPACE_BYTES (\d+)", hdr)
+    assert m and int(m.group(1)) == sv.FORWARD_WORKSPACE_BYTES

@@ -238,3 +238,54 @@ def test_two_group_schedule_matches_plain_schedule(sv, geom, d, bk):
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * 2)
     for h in range(2):
         assert_close(f64_of(o_pp[h]), ref[h][0], f"two-group dense h{h} {geom}")
+
+
+@pytest.mark.parametrize("bq,bk", [(256, 64), (64, 32), (128, 64)])
+def test_schedules_give_identical_results(sv, bq, bk):
+    """The persistent schedule (workspace given) and the static grid, with and
+    without the longest-row-first q-tile order, only change which workgroup
+    runs a q-tile: every output bit is the same in all four runs."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    outs = []
+    for persistent in (True, False):
+        layer = SparseVideoAttention(g, [sv_mask(h) for h in wl.heads], wl.head_dim, bq, bk,
+                                     persistent=persistent)
+        outs.append(layer(q, k, v, scales))
+        for m in layer.maps:
+            m.c.qt_order = None
+        outs.append(layer(q, k, v, scales))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert (bits_of(o) == bits_of(outs[0])).all()
+    ref = _oracle_rows(wl, inp, [np.arange(0, wl.n_tokens, 7)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(outs[0][h][::7]), ref[h][0], f"persistent h{h} {bq}x{bk}")
+
+
+def test_persistent_schedule_over_several_launches(sv):
+    """20 heads take two launches (16 heads each at most) that share one work
+    counter, cleared before each launch; both launches match the static grid
+    bit for bit and the oracle on every row.  Ragged q- and k-tiles."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    kinds = [synth.Head("temporal", radius=1, order="tm"), synth.Head("spatial", window=1),
+             synth.Head("dense"), synth.Head("temporal", radius=2, order="fm")]
+    heads = tuple(kinds[i % 4] for i in range(20))
+    wl = synth.Workload(name="many", seed=17, frames=3, height=5, width=7, head_dim=64,
+                        heads=heads, tiles=((64, 32),))
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    masks = [sv_mask(h) for h in heads]
+    o_p = SparseVideoAttention(g, masks, 64, 64, 32, persistent=True)(q, k, v, scales)
+    o_s = SparseVideoAttention(g, masks, 64, 64, 32, persistent=False)(q, k, v, scales)
+    torch.cuda.synchronize()
+    assert (bits_of(o_p) == bits_of(o_s)).all()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o_p[h]), ref[h][0], f"many h{h}")

@@ -67,6 +67,16 @@ def _compare_map(m, ref, qtiles=None):
         seg = nz_cols[rp[qt]:rp[qt + 1]]
         assert (np.diff(seg) > 0).all()
     assert (cc[:rp[-1]] == cls[np.repeat(np.arange(m.n_qt), np.diff(rp)), nz_cols]).all()
+    # q-tile visiting order: exact against the oracle on whole maps; on sampled
+    # maps a permutation that is longest-row-first with ties by index
+    order = m.qt_order.cpu().numpy()
+    if qtiles is None:
+        assert (order == oracle.qtile_order(rp_ref)).all()
+    assert (np.sort(order) == np.arange(m.n_qt)).all()
+    lens = np.diff(rp.astype(np.int64))[order]
+    assert (np.diff(lens) <= 0).all()
+    ties = np.diff(lens) == 0
+    assert (np.diff(order)[ties] > 0).all()
 
 
 SMALL_CASES = (

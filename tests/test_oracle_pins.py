@@ -364,3 +364,20 @@ def test_headline_tile_rows_match_geometry(kind, w, r, order):
     qtiles = [0, 14, 15, 150, 295]
     cls, *_ = oracle.tile_map(g, kind, w, r, order, 256, 64, qtiles=qtiles)
     assert (cls == _geometric_map(g, kind, w, r, order, 256, 64, qtiles=qtiles)).all()
+
+
+def test_qtile_order_hand_example_and_pairwise_definition():
+    """Longest row first, ties by index: rows of lengths 2, 5, 5, 1, 5 run as
+    1, 2, 4, 0, 3 (worked by hand); on random lengths every pair of positions
+    satisfies the order's definition and the result is a permutation."""
+    rp = np.cumsum([0, 2, 5, 5, 1, 5]).astype(np.int32)
+    assert oracle.qtile_order(rp).tolist() == [1, 2, 4, 0, 3]
+    rng = np.random.default_rng(7)
+    for n in (1, 2, 17, 300):
+        lengths = rng.integers(0, 6, size=n)
+        order = oracle.qtile_order(np.concatenate([[0], np.cumsum(lengths)]))
+        assert sorted(order.tolist()) == list(range(n))
+        for a in range(n):
+            for b in range(a + 1, min(n, a + 40)):
+                la, lb = lengths[order[a]], lengths[order[b]]
+                assert la > lb or (la == lb and order[a] < order[b])
