@@ -35,6 +35,38 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fwd2_kernel_headline_traffic.md")
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the kernel sources (csrc/*.hip, csrc/*.hpp, include/svattn.h)."""
+    import glob
+    import hashlib
+    pkg = os.path.join(ROOT, "block_sparse_spatio_svattn_amd", "csrc")
+    paths = sorted(glob.glob(os.path.join(pkg, "*.hip")) + glob.glob(os.path.join(pkg, "*.hpp")) +
+                   [os.path.join(ROOT, "include", "svattn.h")])
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(os.path.relpath(p, ROOT).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per forward launch from the committed counter summary, or None
+    when there is none for this workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +215,9 @@ def main():
         log(f"naive (every tile masked) {naive_ms:.3f} ms")
         del naive
 
+    traffic = measured_traffic(wl.name) if args.block_q == 256 and args.block_k == 64 else None
+    log(f"traffic per forward launch (committed counters): {traffic}")
+
     # ---- CPU oracle baseline (bounded sample) ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -214,7 +249,9 @@ def main():
         "unpermute_ms": round(unperm_ms, 4),
         "classifier_ms": round(min(cls_ms), 4),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(fwd_tflops / peak, 4), "traffic": None},
+                     "frac": round(fwd_tflops / peak, 4),
+                     # HBM bytes per forward launch (FETCH_SIZE + WRITE_SIZE, calibrated), or null
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         **extra,
     }

@@ -195,3 +195,20 @@ def test_workspace_size_matches_header():
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "svattn.h")).read()
     m = re.search(r"#define SVATTN_FORWARD_WORKSPACE_BYTES (\d+)", hdr)
     assert m and int(m.group(1)) == sv.FORWARD_WORKSPACE_BYTES
+
+
+def test_traffic_summary_parses():
+    """The committed counter summary carries a machine-readable record that
+    bench.py can read (its traffic is reported only for matching sources)."""
+    import json
+    import sys
+    root = os.path.join(os.path.dirname(__file__), "..")
+    text = open(os.path.join(root, "profiles", "fwd2_kernel_headline_traffic.md")).read()
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    assert rec["traffic_bytes_per_launch"] > rec["algorithmic_bytes_per_launch"] > 0
+    assert len(rec["sources_sha256"]) == 64
+    sys.path.insert(0, root)
+    import bench
+    t = bench.measured_traffic("headline")
+    assert t is None or t == rec["traffic_bytes_per_launch"]
+    assert bench.measured_traffic("small") is None
