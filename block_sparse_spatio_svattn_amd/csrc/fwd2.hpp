@@ -129,6 +129,15 @@ __device__ __forceinline__ int key_coord(const Geo& g, int order, int key) {
   return (y << 16) | (p - y * g.W);
 }
 
+// Bits [lo, hi) of a 64-bit word (lo and hi clamped to [0, 64]).
+__device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
+  lo = min(max(lo, 0), 64);
+  hi = min(max(hi, lo), 64);
+  const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
+  return below_hi & ~below_lo;
+}
+
 template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST>
 __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   using C = Cfg<D, BK, NW, QG>;
@@ -233,7 +242,12 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     l_run[gq] = 0.f;
   }
   const float c = hd.scale_log2;
-  const bool need_kc = kind == SVATTN_TEMPORAL;
+  // Keys of a tile fall into runs that share a patch (temporal heads,
+  // temporal-major: runs of F-1 keys) or a patch row (temporal heads,
+  // frame-major: runs of W keys); a lane decides a whole run at once when runs
+  // are at least 16 keys long, else it reads per-key coordinates from LDS.
+  const bool runs_ok = order == SVATTN_TEMPORAL_MAJOR ? g.F - 1 >= 16 : g.W >= 16;
+  const bool need_kc = kind == SVATTN_TEMPORAL && !runs_ok;
 
   // Tile list: the map's CSR row; with a bit mask, every k-tile.
   const int e0 = BITS ? 0 : ld_const(hd.row_ptr + qt);
@@ -366,10 +380,29 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, KPF * QG, 0);
   };
 
-  // Coordinate mask of the tile in stage st (boundary and ragged tiles only),
-  // branch-free.  Key kk of the tile (kk = 32 kb + 8 (i / 4) + 4 hh + i % 4
-  // for accumulator element i) is an anchor key iff kk < P - key0, which can
-  // hold only on the tile that reaches into the first P positions.
+  // Coordinate mask of the tile in stage st (boundary and ragged tiles only).
+  // Key kk of the tile (kk = 32 kb + 8 (i / 4) + 4 hh + i % 4 for accumulator
+  // element i) is an anchor key iff kk < P - key0, which can hold only on the
+  // tile that reaches into the first P positions.  Each lane builds a 64-bit
+  // keep mask of its query over the tile's keys from ranges and runs, then
+  // applies it with one bit extract and one bit select per score.
+  auto apply_keep = [&](int gq, uint64_t m, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      const uint32_t w = (uint32_t)(m >> (32 * kb)) >> (4 * hh);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pos = 8 * (i / 4) + (i % 4);
+        const uint32_t t = (uint32_t)((int)(w << (31 - pos)) >> 31);  // all ones iff kept
+        // (a bit cast straight from a vector element reads element 0 with this
+        // compiler, so the score goes through a scalar first)
+        const float sf = S[kb][gq][i];
+        const uint32_t sb = __builtin_bit_cast(uint32_t, sf);
+        S[kb][gq][i] = __builtin_bit_cast(float, (sb & t) | (0xff800000u & ~t));  // else -inf
+      }
+    }
+  };
+  constexpr int MAXR = BK / 16 + 1;  // runs of >= 16 keys in one tile
   auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
     if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return;
     const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
@@ -388,21 +421,8 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
             S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
           }
         }
-    } else if (kind == SVATTN_SPATIAL) {
-      // kept non-anchor keys: key - mq_a in [0, mq_b)
-#pragma unroll
-      for (int gq = 0; gq < QG; ++gq) {
-        const int base = key0 + lane_kk - mq_a[gq];
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = kb * 32 + 8 * (i / 4) + (i % 4);
-            const bool keep = ((uint32_t)(base + kk) < (uint32_t)mq_b[gq]) | (kk + lane_kk < lim_anchor);
-            S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
-          }
-      }
-    } else if (kind == SVATTN_TEMPORAL) {
+    } else if (kind == SVATTN_TEMPORAL && !runs_ok) {
+      // short runs: per-key patch coordinates from LDS
       const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
       const bool any_anchor = lim_anchor > 0;
 #pragma unroll
@@ -424,15 +444,64 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
           }
         }
       }
-    } else {  // dense: only the key range
+    } else {
+      const uint64_t in_range = bit_range(0, lim_n);
+      const uint64_t anchor = bit_range(0, lim_anchor);
+      uint64_t keep[QG];
+      if (kind == SVATTN_SPATIAL) {
+        // kept non-anchor keys: [mq_a, mq_a + mq_b)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+        for (int gq = 0; gq < QG; ++gq) keep[gq] = bit_range(mq_a[gq] - key0, mq_a[gq] + mq_b[gq] - key0) | anchor;
+      } else if (kind == SVATTN_TEMPORAL) {
+        const int r = hd.radius;
+        const uint32_t r2 = 2u * (uint32_t)r;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool keep = kb * 32 + 8 * (i / 4) + (i % 4) + lane_kk < lim_n;
+        for (int gq = 0; gq < QG; ++gq) keep[gq] = anchor;
+        const int s0 = max(key0, g.P) - key0;  // first non-anchor key of the tile
+        const int e0 = min(BK, lim_n);         // past the last key of the tile
+        if (s0 < e0) {
+          if (order == SVATTN_TEMPORAL_MAJOR) {
+            // run: the F-1 frames of one patch
+            const int F1 = g.F - 1;
+            int p = (int)g.divF1.div((uint32_t)(s0 + key0 - g.P));
+            int rs = s0, re = g.P + (p + 1) * F1 - key0;
 #pragma unroll
-          for (int gq = 0; gq < QG; ++gq) S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
+            for (int i = 0; i < MAXR; ++i) {
+              const int y = (int)g.divW.div((uint32_t)p), x = p - y * g.W;
+              const uint64_t rb = bit_range(rs, min(re, e0));
+#pragma unroll
+              for (int gq = 0; gq < QG; ++gq) {
+                const bool k = ((uint32_t)(y - mq_a[gq] + r) <= r2) & ((uint32_t)(x - mq_b[gq] + r) <= r2);
+                keep[gq] |= k ? rb : 0ull;
+              }
+              ++p;
+              rs = re;
+              re += F1;
+            }
+          } else {
+            // run: one patch row of one frame; x advances with the key
+            int rs = s0;
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i) {
+              const int pp = (int)g.divP.mod((uint32_t)(key0 + rs));
+              const int y = (int)g.divW.div((uint32_t)pp), x0 = pp - y * g.W;
+              const int re = min(rs + (g.W - x0), e0);
+#pragma unroll
+              for (int gq = 0; gq < QG; ++gq) {
+                const bool ky = (uint32_t)(y - mq_a[gq] + r) <= r2;
+                const int lo = rs + (mq_b[gq] - r - x0), hi = rs + (mq_b[gq] + r + 1 - x0);
+                keep[gq] |= ky ? bit_range(max(lo, rs), min(hi, re)) : 0ull;
+              }
+              rs = max(re, rs);
+            }
+          }
         }
+      } else {
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) keep[gq] = ~0ull;  // dense: only the key range
+      }
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq] & in_range, S);
     }
   };
 

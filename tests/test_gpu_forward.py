@@ -289,3 +289,28 @@ def test_persistent_schedule_over_several_launches(sv):
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
     for h in range(wl.n_heads):
         assert_close(f64_of(o_p[h]), ref[h][0], f"many h{h}")
+
+
+@pytest.mark.parametrize("geom,r,order,bq,bk", [
+    ((17, 3, 5), 1, "tm", 64, 64),    # F-1 = 16: patch runs of 16 keys, ragged tail (N = 255)
+    ((21, 4, 6), 1, "tm", 256, 64),   # F-1 = 20, as the headline; N = 504
+    ((21, 4, 6), 2, "tm", 64, 32),
+    ((17, 3, 16), 1, "fm", 128, 64),  # W = 16: patch-row runs, frame-major
+    ((5, 6, 40), 3, "fm", 64, 32),
+    ((3, 2, 70), 9, "fm", 256, 64),   # rows longer than a tile
+])
+def test_long_run_masks_all_rows(sv, geom, r, order, bq, bk):
+    """Geometries whose key runs (F-1 frames of a patch in temporal-major order,
+    W patches of a row in frame-major order) are at least 16 keys long, so
+    boundary tiles take the run-mask path; every output row against the
+    oracle, with spatial and dense heads beside them."""
+    F, H, W = geom
+    heads = (synth.Head("temporal", radius=r, order=order), synth.Head("spatial", window=1),
+             synth.Head("temporal", radius=0, order=order), synth.Head("dense"))
+    wl = synth.Workload(name="runs", seed=23, frames=F, height=H, width=W, head_dim=128,
+                        heads=heads, tiles=((bq, bk),))
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, bq, bk)
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"runs {geom} r{r} {order} h{h} {bq}x{bk}")
