@@ -81,6 +81,8 @@ def main():
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="forward launches timed after a 512 MB write that evicts L2 and MALL (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -215,6 +217,23 @@ def main():
         log(f"naive (every tile masked) {naive_ms:.3f} ms")
         del naive
 
+    # ---- forward after evicting the caches: a 512 MB write between launches ----
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+        cm = []
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xff)
+            a, b = ev(), ev()
+            a.record(stream)
+            layer.attend(q, k, v, out, scales)
+            b.record(stream)
+            cm.append((a, b))
+        torch.cuda.synchronize()
+        cold_ms = round(float(np.mean([a.elapsed_time(b) for a, b in cm])), 4)
+        log(f"forward after a 512 MB cache-evicting write: {cold_ms:.3f} ms")
+        del flush
+
     traffic = measured_traffic(wl.name) if args.block_q == 256 and args.block_k == 64 else None
     log(f"traffic per forward launch (committed counters): {traffic}")
 
@@ -244,7 +263,10 @@ def main():
                    "temporal_order": args.temporal_order, "kept_fraction": round(kept_frac, 6),
                    "parallelism": "single-gpu"},
         "fwd_kernel": {"ms": round(fwd_ms, 4), "ms_min": round(float(fwd_all.min()), 4),
-                       "tflops": round(fwd_tflops, 2), "pct_bf16_peak": round(100 * fwd_tflops / peak, 2)},
+                       "ms_median": round(float(np.median(fwd_all)), 4),
+                       "ms_p90": round(float(np.percentile(fwd_all, 90)), 4),
+                       "tflops": round(fwd_tflops, 2), "pct_bf16_peak": round(100 * fwd_tflops / peak, 2),
+                       **({"ms_cold_cache": cold_ms} if cold_ms is not None else {})},
         "permute_ms": round(perm_ms, 4),
         "unpermute_ms": round(unperm_ms, 4),
         "classifier_ms": round(min(cls_ms), 4),
