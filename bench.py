@@ -79,6 +79,7 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-aligned", action="store_true", help="skip the tile-aligned traversal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -216,6 +217,38 @@ def main():
         extra["naive_all_boundary"] = {"ms": round(naive_ms, 4), "slowdown_vs_full_boundary": round(naive_ms / fwd_ms, 3)}
         log(f"naive (every tile masked) {naive_ms:.3f} ms")
         del naive
+
+    # ---- tile-aligned traversal: every non-empty tile full (a different mask) ----
+    if not args.no_aligned:
+        aligned = SparseVideoAttention(g, masks, D, args.block_q, args.block_k, map_flags=sv.MAP_TILE_ALIGNED)
+        aligned.permute_inputs(q, k, v)
+        aligned.attend(q, k, v, out, scales)
+        torch.cuda.synchronize()
+        am = []
+        for _ in range(max(3, args.dense_steps)):
+            a, b = ev(), ev()
+            a.record(stream)
+            aligned.attend(q, k, v, out, scales)
+            b.record(stream)
+            am.append((a, b))
+        torch.cuda.synchronize()
+        aligned_ms = float(np.mean([a.elapsed_time(b) for a, b in am]))
+        # kept pairs of the snapped mask: the in-range area of every listed tile
+        pairs = 0
+        for mp in aligned.maps:
+            nnz = mp.nnz()
+            rp = mp.row_ptr.cpu().numpy().astype(np.int64)
+            col = mp.col[:nnz].cpu().numpy().astype(np.int64)
+            rows = np.minimum(args.block_q, N - np.arange(mp.n_qt) * args.block_q)
+            cols = np.minimum(args.block_k, N - col * args.block_k)
+            cs = np.concatenate([[0], np.cumsum(cols)])
+            pairs += int((cs[rp[1:]] - cs[rp[:-1]]) @ rows)
+        extra["tile_aligned"] = {"ms": round(aligned_ms, 4), "kept_pairs": pairs,
+                                 "tflops_on_kept": round(4 * D * pairs / (aligned_ms * 1e-3) / 1e12, 2)}
+        if "dense" in extra:
+            extra["tile_aligned"]["speedup_vs_dense"] = round(extra["dense"]["ms"] / aligned_ms, 3)
+        log(f"tile-aligned traversal {aligned_ms:.3f} ms ({pairs} kept pairs)")
+        del aligned
 
     # ---- forward after evicting the caches: a 512 MB write between launches ----
     cold_ms = None

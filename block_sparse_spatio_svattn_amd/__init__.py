@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR",
-    "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "FORWARD_WORKSPACE_BYTES",
+    "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "MAP_TILE_ALIGNED", "FORWARD_WORKSPACE_BYTES",
     "new_workspace",
     "SvattnError", "Geom", "Mask", "TileMap", "lib", "version",
     "tile_map_dims", "build_tile_map", "permutation_index", "permute_tokens",
@@ -32,6 +32,7 @@ SPATIAL, TEMPORAL, DENSE = 0, 1, 2
 FRAME_MAJOR, TEMPORAL_MAJOR = 0, 1
 TILE_EMPTY, TILE_BOUNDARY, TILE_FULL = 0, 1, 2
 MAP_ALL_BOUNDARY = 1
+MAP_TILE_ALIGNED = 2
 FORWARD_WORKSPACE_BYTES = 256  # SVATTN_FORWARD_WORKSPACE_BYTES
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvattn.so")

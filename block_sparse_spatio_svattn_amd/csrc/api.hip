@@ -157,7 +157,10 @@ int svattn_build_tile_map_ex(const svattn_geom* geom, const svattn_mask* mask, s
   if (s) return s;
   if ((s = check_mask(mask))) return s;
   if (!map) return fail(SVATTN_ERR_INVALID_ARG, "map is NULL");
-  if (flags & ~SVATTN_MAP_ALL_BOUNDARY) return fail(SVATTN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~(SVATTN_MAP_ALL_BOUNDARY | SVATTN_MAP_TILE_ALIGNED))
+    return fail(SVATTN_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & SVATTN_MAP_ALL_BOUNDARY) && (flags & SVATTN_MAP_TILE_ALIGNED))
+    return fail(SVATTN_ERR_INVALID_ARG, "ALL_BOUNDARY and TILE_ALIGNED exclude each other");
   if (!map_bq_ok(map->block_q) || !map_bk_ok(map->block_k))
     return fail(SVATTN_ERR_UNSUPPORTED, "tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64,128}",
                 map->block_q, map->block_k);

@@ -408,6 +408,10 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
     const int lim_n = N - key0;           // kk >= lim_n: past the last token
     const int lane_kk = 4 * hh;
+    // A full tile that runs past the last token keeps every in-range pair:
+    // only the key range applies (with tile-aligned maps it keeps pairs the
+    // coordinate mask would drop).
+    const int mkind = cls == SVATTN_TILE_BOUNDARY ? kind : SVATTN_DENSE;
     if constexpr (BITS) {
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq)
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
             S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
           }
         }
-    } else if (kind == SVATTN_TEMPORAL && !runs_ok) {
+    } else if (mkind == SVATTN_TEMPORAL && !runs_ok) {
       // short runs: per-key patch coordinates from LDS
       const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
       const bool any_anchor = lim_anchor > 0;
@@ -448,11 +452,11 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
       const uint64_t in_range = bit_range(0, lim_n);
       const uint64_t anchor = bit_range(0, lim_anchor);
       uint64_t keep[QG];
-      if (kind == SVATTN_SPATIAL) {
+      if (mkind == SVATTN_SPATIAL) {
         // kept non-anchor keys: [mq_a, mq_a + mq_b)
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) keep[gq] = bit_range(mq_a[gq] - key0, mq_a[gq] + mq_b[gq] - key0) | anchor;
-      } else if (kind == SVATTN_TEMPORAL) {
+      } else if (mkind == SVATTN_TEMPORAL) {
         const int r = hd.radius;
         const uint32_t r2 = 2u * (uint32_t)r;
 #pragma unroll

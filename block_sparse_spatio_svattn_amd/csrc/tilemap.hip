@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(Geo g, svattn_mask m
     const int c0 = kt * map.block_k, c1 = min(g.N, c0 + map.block_k);
     uint8_t c = classify(g, m, r0, r1, c0, c1);
     if ((flags & SVATTN_MAP_ALL_BOUNDARY) && c != SVATTN_TILE_EMPTY) c = SVATTN_TILE_BOUNDARY;
+    if ((flags & SVATTN_MAP_TILE_ALIGNED) && c != SVATTN_TILE_EMPTY) c = SVATTN_TILE_FULL;
     map.cls[(size_t)qt * map.n_kt + kt] = c;
     count += (c != SVATTN_TILE_EMPTY);
   }

@@ -74,6 +74,11 @@ extern "C" {
 /* Flags for svattn_build_tile_map_ex. */
 #define SVATTN_MAP_ALL_BOUNDARY 1u  /* mark every non-empty tile BOUNDARY (the naive
                                        traversal that masks every visited tile) */
+#define SVATTN_MAP_TILE_ALIGNED 2u  /* mark every non-empty tile FULL: the mask snapped to
+                                       the tiles (ainews.tenesys.com, "W skrócie" and item 4
+                                       of its list; oossa.com, body paragraph 1), read as:
+                                       every pair of a tile that holds a kept pair is kept.
+                                       The result then depends on block_q x block_k. */
 
 typedef struct {
   int32_t frames, height, width; /* F, H, W >= 1; N = F*H*W < 2^31 / 256 */
@@ -125,7 +130,8 @@ SVATTN_API int svattn_tile_map_dims(const svattn_geom* geom, int32_t block_q, in
  * classes are derived from the token coordinates of each block, not sampled.
  * map->block_q/block_k/n_qt/n_kt must be set (n_qt/n_kt as from
  * svattn_tile_map_dims).  The map depends only on (geom, mask, tile shape) and
- * can be reused across calls.  Spatial heads must be FRAME_MAJOR.
+ * can be reused across calls.  Spatial heads must be FRAME_MAJOR.  flags: 0,
+ * SVATTN_MAP_ALL_BOUNDARY or SVATTN_MAP_TILE_ALIGNED (not both).
  */
 SVATTN_API int svattn_build_tile_map(const svattn_geom* geom, const svattn_mask* mask,
                           svattn_tile_map* map, void* stream);

@@ -49,6 +49,7 @@ from .core import (  # noqa: F401
     tile_counts,
     tile_map,
     qtile_order,
+    tile_aligned_keep,
     attend_rows,
     attend_head,
     unpermute_rows,

@@ -175,6 +175,30 @@ def qtile_order(row_ptr: np.ndarray) -> np.ndarray:
     return np.argsort(-lengths, kind="stable").astype(np.int32)
 
 
+def tile_aligned_keep(g: Geometry, kind: str, window: int, radius: int, order: str,
+                      block_q: int, block_k: int, rows: np.ndarray) -> np.ndarray:
+    """Mask snapped to the tiles of a head's layout (the final tile-aligned
+    traversal of the tenesys page, "W skrócie" and item 4 of its list; oossa
+    page, body paragraph 1).  The pages give no rule; the reading here: a tile
+    of block_q x block_k layout positions that holds at least one kept pair is
+    kept whole, any other tile is dropped, so no pair of the exact mask is lost.
+
+    Returns keep[i, j] for frame-major query tokens ``rows`` and all frame-major
+    key tokens.
+    """
+    toks = layout_tokens(g, order)
+    pos = np.empty(g.n, dtype=np.int64)
+    pos[toks] = np.arange(g.n)                       # layout position of each token
+    rows = np.asarray(rows)
+    q_tile = pos[rows] // block_q
+    tiles = np.unique(q_tile)
+    counts, _ = tile_counts(g, kind, window, radius, order, block_q, block_k, qtiles=tiles)
+    nonempty = counts > 0                            # [len(tiles), n_kt]
+    row_of = np.searchsorted(tiles, q_tile)
+    k_tile = pos // block_k                          # k-tile of each key token
+    return nonempty[row_of][:, k_tile]
+
+
 # ---------------------------------------------------------------------------
 # Attention (aihirek page, SVG section paragraph 1: softmax attention over the
 # kept pairs).  O = softmax(S + M) V with S = Q K^T * scale, M = 0 or -inf.
@@ -198,11 +222,14 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 def attend_head(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray, scale: float,
                 g: Geometry, kind: str, window: int, radius: int,
-                rows: Optional[np.ndarray] = None, block: int = 256):
+                rows: Optional[np.ndarray] = None, block: int = 256,
+                tile_aligned: Optional[Tuple[str, int, int]] = None):
     """Attention of one head in frame-major order.
 
     qb, kb, vb: bf16 bit patterns [N, d].  ``rows``: frame-major query tokens to
-    compute (default all).  Returns (O [len(rows), d] float64, lse float64).
+    compute (default all).  ``tile_aligned`` = (order, block_q, block_k) uses the
+    tile-snapped mask of ``tile_aligned_keep`` instead of the exact one.
+    Returns (O [len(rows), d] float64, lse float64).
     """
     k = bf16_to_f64(kb)
     v = bf16_to_f64(vb)
@@ -213,7 +240,10 @@ def attend_head(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray, scale: float,
     sc = float(np.float32(scale))
     for s in range(0, len(rows), block):
         rr = rows[s:s + block]
-        keep = keep_matrix(g, kind, window, radius, rr, cols)
+        if tile_aligned is None:
+            keep = keep_matrix(g, kind, window, radius, rr, cols)
+        else:
+            keep = tile_aligned_keep(g, kind, window, radius, *tile_aligned, rr)
         o[s:s + block], lse[s:s + block] = attend_rows(bf16_to_f64(qb[rr]), k, v, sc, keep)
     return o, lse
 

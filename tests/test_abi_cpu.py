@@ -90,6 +90,7 @@ def test_build_tile_map_validation():
         (good_mask, _map(g, 64, 64, row_ptr=FAKE + 2), 0, INVALID),             # misaligned
         (good_mask, _map(g, 64, 64, qt_order=FAKE + 2), 0, INVALID),            # misaligned order
         (good_mask, _map(g, 64, 64), 4, INVALID),                               # unknown flag
+        (good_mask, _map(g, 64, 64), 3, INVALID),                               # both traversal flags
     ]
     for m, mp, flags, want in cases:
         got = L.svattn_build_tile_map_ex(ctypes.byref(g), ctypes.byref(m), ctypes.byref(mp), flags, None)

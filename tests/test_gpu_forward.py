@@ -314,3 +314,34 @@ def test_long_run_masks_all_rows(sv, geom, r, order, bq, bk):
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
     for h in range(wl.n_heads):
         assert_close(f64_of(o[h]), ref[h][0], f"runs {geom} r{r} {order} h{h} {bq}x{bk}")
+
+
+@pytest.mark.parametrize("wl_name,bq,bk", [("tiny", 32, 32), ("tiny", 256, 64), ("small", 128, 64), ("small", 64, 32)])
+def test_tile_aligned_traversal_all_rows(sv, wl_name, bq, bk):
+    """Maps built with MAP_TILE_ALIGNED mark every non-empty tile full, so the
+    forward attends to every pair of those tiles; every output row against the
+    oracle's tile-snapped mask in each head's own token order."""
+    wl = synth.WORKLOADS[wl_name]
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, bq, bk, flags=sv.MAP_TILE_ALIGNED)
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+    for h, head in enumerate(wl.heads):
+        ref, _ = oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind, head.window,
+                                    head.radius, tile_aligned=(head.order, bq, bk))
+        assert_close(f64_of(o[h]), ref, f"tile-aligned {wl_name} h{h} {bq}x{bk}")
+
+
+def test_tile_aligned_long_runs(sv):
+    """Tile snapping with key runs of 20 frames (the headline's F - 1) and a
+    ragged tail, temporal-major and frame-major temporal heads."""
+    heads = (synth.Head("temporal", radius=1, order="tm"), synth.Head("temporal", radius=2, order="fm"),
+             synth.Head("spatial", window=1))
+    wl = synth.Workload(name="ta", seed=29, frames=21, height=4, width=6, head_dim=128, heads=heads,
+                        tiles=((128, 64),))
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, 128, 64, flags=sv.MAP_TILE_ALIGNED)
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+    for h, head in enumerate(heads):
+        ref, _ = oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind, head.window,
+                                    head.radius, tile_aligned=(head.order, 128, 64))
+        assert_close(f64_of(o[h]), ref, f"tile-aligned long runs h{h}")

@@ -129,3 +129,20 @@ def test_all_boundary_flag(sv):
     ca, cb = a.cls.cpu().numpy(), b.cls.cpu().numpy()
     assert ((ca != 0) == (cb != 0)).all() and set(np.unique(cb)) <= {0, 1}
     assert (a.row_ptr.cpu().numpy() == b.row_ptr.cpu().numpy()).all()
+
+
+def test_tile_aligned_flag_map(sv):
+    """MAP_TILE_ALIGNED lists the same non-empty tiles as the exact map, every
+    one FULL."""
+    g = sv.Geom(5, 24, 40)
+    for head in (synth.Head("temporal", radius=2, order="tm"), synth.Head("spatial", window=1)):
+        a = sv.build_tile_map(g, sv_mask(head), 128, 64)
+        b = sv.build_tile_map(g, sv_mask(head), 128, 64, flags=sv.MAP_TILE_ALIGNED)
+        torch.cuda.synchronize()
+        ca, cb = a.cls.cpu().numpy(), b.cls.cpu().numpy()
+        assert ((ca != 0) == (cb != 0)).all()
+        assert set(np.unique(cb).tolist()) <= {0, 2}
+        nnz = a.nnz()
+        assert nnz == b.nnz()
+        assert (a.col[:nnz].cpu().numpy() == b.col[:nnz].cpu().numpy()).all()
+        assert (b.col_cls[:nnz].cpu().numpy() == 2).all()

@@ -381,3 +381,57 @@ def test_qtile_order_hand_example_and_pairwise_definition():
             for b in range(a + 1, min(n, a + 40)):
                 la, lb = lengths[order[a]], lengths[order[b]]
                 assert la > lb or (la == lb and order[a] < order[b])
+
+
+def _brute_tile_aligned(g, kind, w, r, order, bq, bk):
+    """Pure-Python tile snapping over every pair of a tiny geometry, written
+    from the definition (no numpy mask routines): a tile of layout positions is
+    kept whole iff some pair in it is kept."""
+    F, H, W = g.frames, g.height, g.width
+    P, n = H * W, F * H * W
+    if order == "fm":
+        toks = list(range(n))
+    else:
+        toks = list(range(P)) + [f * P + p for p in range(P) for f in range(1, F)]
+    def keep(i, j):
+        fi, pi = divmod(i, P)
+        fj, pj = divmod(j, P)
+        if fj == 0 or kind == "dense":
+            return True
+        if kind == "spatial":
+            return abs(fi - fj) <= w
+        (yi, xi), (yj, xj) = divmod(pi, W), divmod(pj, W)
+        return max(abs(yi - yj), abs(xi - xj)) <= r
+    out = [[False] * n for _ in range(n)]
+    for a0 in range(0, n, bq):
+        for b0 in range(0, n, bk):
+            cells = [(toks[a], toks[b]) for a in range(a0, min(n, a0 + bq)) for b in range(b0, min(n, b0 + bk))]
+            hit = any(keep(i, j) for i, j in cells)
+            for i, j in cells:
+                out[i][j] = hit
+    return np.array(out)
+
+
+@pytest.mark.parametrize("kind,w,r,order,bq,bk", [("temporal", 0, 1, "tm", 16, 16), ("temporal", 0, 1, "fm", 16, 8),
+                                                  ("spatial", 1, 0, "fm", 8, 16), ("temporal", 0, 0, "tm", 32, 16)])
+def test_tile_aligned_mask_brute_force(kind, w, r, order, bq, bk):
+    """The tile-snapped mask equals a pure-Python snapping on a tiny geometry
+    with ragged tiles, contains the exact mask, and keeps whole tiles."""
+    g = Geometry(3, 4, 4)   # N = 48
+    got = oracle.tile_aligned_keep(g, kind, w, r, order, bq, bk, np.arange(g.n))
+    want = _brute_tile_aligned(g, kind, w, r, order, bq, bk)
+    assert (got == want).all()
+    exact = oracle.keep_matrix(g, kind, w, r, np.arange(g.n), np.arange(g.n))
+    assert (got >= exact).all()
+
+
+def test_tile_aligned_equals_exact_on_frame_aligned_tiles():
+    """Tiles that divide the frame hold one (query frame, key frame) pair each,
+    so a spatial mask is already tile-aligned: snapping changes nothing, while a
+    temporal mask on the same tiles gains pairs."""
+    g = Geometry(4, 8, 8)
+    rows = np.arange(g.n)
+    sp = oracle.tile_aligned_keep(g, "spatial", 1, 0, "fm", 32, 32, rows)
+    assert (sp == oracle.keep_matrix(g, "spatial", 1, 0, rows, rows)).all()
+    tp = oracle.tile_aligned_keep(g, "temporal", 0, 1, "tm", 32, 32, rows)
+    assert tp.sum() > oracle.keep_matrix(g, "temporal", 0, 1, rows, rows).sum()
