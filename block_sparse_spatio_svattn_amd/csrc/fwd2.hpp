@@ -403,8 +403,11 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     }
   };
   constexpr int MAXR = BK / 16 + 1;  // runs of >= 16 keys in one tile
-  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
-    if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return;
+  // Returns (the same for the whole wave) 2 if every score of the wave's
+  // queries is masked (the tile changes nothing for them: softmax and P V can
+  // be skipped), 1 if none is, 0 otherwise.
+  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) -> int {
+    if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return 1;
     const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
     const int lim_n = N - key0;           // kk >= lim_n: past the last token
     const int lane_kk = 4 * hh;
@@ -425,6 +428,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
             S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
           }
         }
+      return 0;
     } else if (mkind == SVATTN_TEMPORAL && !runs_ok) {
       // short runs: per-key patch coordinates from LDS
       const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
@@ -448,6 +452,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
           }
         }
       }
+      return 0;
     } else {
       const uint64_t in_range = bit_range(0, lim_n);
       const uint64_t anchor = bit_range(0, lim_anchor);
@@ -504,8 +509,18 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) keep[gq] = ~0ull;  // dense: only the key range
       }
+      bool none = true, all = true;
 #pragma unroll
-      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq] & in_range, S);
+      for (int gq = 0; gq < QG; ++gq) {
+        keep[gq] &= in_range;
+        none &= keep[gq] == 0ull;
+        all &= keep[gq] == ~0ull;
+      }
+      if (__all(none)) return 2;
+      if (__all(all)) return 1;
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
+      return 0;
     }
   };
 
@@ -634,14 +649,14 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
           mfma_work(j, sj, sp);
           __syncthreads();
           if (j < n) {
-            mask(sj, key_c, cls_c, S);
+            (void)mask(sj, key_c, cls_c, S);
             softmax(S, P, [](int) {});
           }
         } else {
           if (j >= 1) {
             const bool dma = j + 1 < n;
             if (dma) issue_kc(key_n, sn);
-            mask(sp, key_p, cls_p, S);
+            (void)mask(sp, key_p, cls_p, S);
             softmax(S, P, [&](int ch) { dma_in_softmax(ch, dma, key_n, sn); });
           }
           __syncthreads();
@@ -669,12 +684,13 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
       int key_nn = 0, cls_nn = 0;
       fetch(j + 2, key_nn, cls_nn);
       qk(st, S, [](int) {});
-      mask(st, key_c, cls_c, S);
-      softmax(S, P, [](int) {});
+      // a wave whose queries keep no key of this tile skips its softmax and P V
+      const int ms = mask(st, key_c, cls_c, S);
+      if (ms != 2) softmax(S, P, [](int) {});
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < n) issue(key_n, next_stage(st));
       __builtin_amdgcn_sched_barrier(0);
-      pv(st, P, [](int) {});
+      if (ms != 2) pv(st, P, [](int) {});
       wait_tiles();
       __syncthreads();
       key_c = key_n; cls_c = cls_n;
