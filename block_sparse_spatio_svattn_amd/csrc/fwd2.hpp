@@ -403,60 +403,26 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     }
   };
   constexpr int MAXR = BK / 16 + 1;  // runs of >= 16 keys in one tile
-  // Returns (the same for the whole wave) 2 if every score of the wave's
-  // queries is masked (the tile changes nothing for them: softmax and P V can
-  // be skipped), 1 if none is, 0 otherwise.
-  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) -> int {
+  // Mask plan of the tile starting at key0, from coordinates only (so it can
+  // run before the tile's scores exist).  Returns, the same for the whole
+  // wave: 1 if no score needs masking (not a boundary or ragged tile, or every
+  // pair kept), 2 if every score of the wave's queries is masked (the tile
+  // changes nothing for them: S, softmax and P V are skipped), 0 if the keep
+  // masks in keep[] must be applied, 3 if the per-score test (bit-mask input,
+  // or temporal heads with short key runs) must run on the scores.
+  auto plan = [&](int key0, int cls, uint64_t (&keep)[QG]) __attribute__((always_inline)) -> int {
     if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return 1;
     const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
     const int lim_n = N - key0;           // kk >= lim_n: past the last token
-    const int lane_kk = 4 * hh;
     // A full tile that runs past the last token keeps every in-range pair:
     // only the key range applies (with tile-aligned maps it keeps pairs the
     // coordinate mask would drop).
     const int mkind = cls == SVATTN_TILE_BOUNDARY ? kind : SVATTN_DENSE;
-    if constexpr (BITS) {
-#pragma unroll
-      for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          const uint32_t word = kb * 32 < lim_n ? bits_row[gq][(key0 >> 5) + kb] : 0u;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = kb * 32 + 8 * (i / 4) + (i % 4) + lane_kk;
-            const bool keep = ((word >> (kk & 31)) & 1u) & (kk < lim_n);
-            S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
-          }
-        }
-      return 0;
-    } else if (mkind == SVATTN_TEMPORAL && !runs_ok) {
-      // short runs: per-key patch coordinates from LDS
-      const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
-      const bool any_anchor = lim_anchor > 0;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int kk0 = kb * 32 + 8 * i4 + lane_kk;
-          const int4 kc4 = *(const int4*)&kcs[st][kk0];
-          const int kcv[4] = {kc4.x, kc4.y, kc4.z, kc4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int yk = kcv[j] >> 16, xk = kcv[j] & 0xffff;
-            const bool anchor = any_anchor & (kk0 + j < lim_anchor);
-#pragma unroll
-            for (int gq = 0; gq < QG; ++gq) {
-              const bool keep = (((uint32_t)(yk - mq_a[gq]) + r <= r2) & ((uint32_t)(xk - mq_b[gq]) + r <= r2)) | anchor;
-              S[kb][gq][i4 * 4 + j] = keep ? S[kb][gq][i4 * 4 + j] : -INFINITY;
-            }
-          }
-        }
-      }
-      return 0;
-    } else {
+    if constexpr (BITS) return 3;
+    if (mkind == SVATTN_TEMPORAL && !runs_ok) return 3;
+    {
       const uint64_t in_range = bit_range(0, lim_n);
       const uint64_t anchor = bit_range(0, lim_anchor);
-      uint64_t keep[QG];
       if (mkind == SVATTN_SPATIAL) {
         // kept non-anchor keys: [mq_a, mq_a + mq_b)
 #pragma unroll
@@ -518,10 +484,65 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
       }
       if (__all(none)) return 2;
       if (__all(all)) return 1;
-#pragma unroll
-      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
       return 0;
     }
+  };
+
+
+  // Per-score test of a boundary tile (plan() returned 3).
+  auto mask_scores = [&](int st, int key0, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
+    const int lim_anchor = g.P - key0;
+    const int lim_n = N - key0;
+    const int lane_kk = 4 * hh;
+    if constexpr (BITS) {
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const uint32_t word = kb * 32 < lim_n ? bits_row[gq][(key0 >> 5) + kb] : 0u;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = kb * 32 + 8 * (i / 4) + (i % 4) + lane_kk;
+            const bool keep = ((word >> (kk & 31)) & 1u) & (kk < lim_n);
+            S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
+          }
+        }
+    } else {
+      // short runs: per-key patch coordinates from LDS
+      const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
+      const bool any_anchor = lim_anchor > 0;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int kk0 = kb * 32 + 8 * i4 + lane_kk;
+          const int4 kc4 = *(const int4*)&kcs[st][kk0];
+          const int kcv[4] = {kc4.x, kc4.y, kc4.z, kc4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int yk = kcv[j] >> 16, xk = kcv[j] & 0xffff;
+            const bool anchor = any_anchor & (kk0 + j < lim_anchor);
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq) {
+              const bool keep = (((uint32_t)(yk - mq_a[gq]) + r <= r2) & ((uint32_t)(xk - mq_b[gq]) + r <= r2)) | anchor;
+              S[kb][gq][i4 * 4 + j] = keep ? S[kb][gq][i4 * 4 + j] : -INFINITY;
+            }
+          }
+        }
+      }
+    }
+  };
+  // plan + apply in one step (the two-group schedule).
+  auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) -> int {
+    uint64_t keep[QG];
+    const int m = plan(key0, cls, keep);
+    if (m == 0) {
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
+    } else if (m == 3) {
+      mask_scores(st, key0, S);
+    }
+    return m;
   };
 
   // Online softmax of one tile's scores; P (bf16) is the B operand of P V.
@@ -683,10 +704,19 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     for (int j = 0; j < n; ++j) {
       int key_nn = 0, cls_nn = 0;
       fetch(j + 2, key_nn, cls_nn);
-      qk(st, S, [](int) {});
-      // a wave whose queries keep no key of this tile skips its softmax and P V
-      const int ms = mask(st, key_c, cls_c, S);
-      if (ms != 2) softmax(S, P, [](int) {});
+      // a wave whose queries keep no key of this tile skips S, softmax and P V
+      uint64_t keep[QG];
+      const int ms = plan(key_c, cls_c, keep);
+      if (ms != 2) {
+        qk(st, S, [](int) {});
+        if (ms == 0) {
+#pragma unroll
+          for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
+        } else if (ms == 3) {
+          mask_scores(st, key_c, S);
+        }
+        softmax(S, P, [](int) {});
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < n) issue(key_n, next_stage(st));
       __builtin_amdgcn_sched_barrier(0);
