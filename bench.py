@@ -80,6 +80,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-aligned", action="store_true", help="skip the tile-aligned traversal")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-permutation step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -217,6 +218,25 @@ def main():
         extra["naive_all_boundary"] = {"ms": round(naive_ms, 4), "slowdown_vs_full_boundary": round(naive_ms / fwd_ms, 3)}
         log(f"naive (every tile masked) {naive_ms:.3f} ms")
         del naive
+
+    # ---- the step with the permutation fused into the forward (no separate passes) ----
+    if not args.no_fused:
+        fused = SparseVideoAttention(g, masks, D, args.block_q, args.block_k, fused=True)
+        fused(q, k, v, scales, out=out)
+        torch.cuda.synchronize()
+        fm = []
+        for _ in range(max(3, args.dense_steps)):
+            a, b = ev(), ev()
+            a.record(stream)
+            fused(q, k, v, scales, out=out)
+            b.record(stream)
+            fm.append((a, b))
+        torch.cuda.synchronize()
+        fused_ms = float(np.mean([a.elapsed_time(b) for a, b in fm]))
+        extra["fused_step"] = {"ms": round(fused_ms, 4), "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                               "vs_separate_step": round(ms_step / fused_ms, 3)}
+        log(f"step with the permutation fused into the forward {fused_ms:.3f} ms")
+        del fused
 
     # ---- tile-aligned traversal: every non-empty tile full (a different mask) ----
     if not args.no_aligned:

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR",
     "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "MAP_TILE_ALIGNED", "FORWARD_WORKSPACE_BYTES",
-    "new_workspace",
+    "new_workspace", "forward_fused",
     "SvattnError", "Geom", "Mask", "TileMap", "lib", "version",
     "tile_map_dims", "build_tile_map", "permutation_index", "permute_tokens",
     "unpermute", "forward", "forward_ptrs", "forward_dense_mask",
@@ -99,11 +99,13 @@ def lib() -> ctypes.CDLL:
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.svattn_forward_ptrs.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
                                       P(_vp), P(_vp), P(_vp), P(_vp), P(_vp), _vp, _vp]
+    L.svattn_forward_fused.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.svattn_forward_dense_mask.argtypes = [_i32, _i32, _i32, _vp, _i32, P(ctypes.c_float),
                                             _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     for f in ("svattn_tile_map_dims", "svattn_build_tile_map", "svattn_build_tile_map_ex",
               "svattn_permutation_index", "svattn_permute_tokens", "svattn_unpermute",
-              "svattn_forward", "svattn_forward_ptrs", "svattn_forward_dense_mask"):
+              "svattn_forward", "svattn_forward_ptrs", "svattn_forward_fused", "svattn_forward_dense_mask"):
         getattr(L, f).restype = ctypes.c_int
     _LIB = L
     return L
@@ -261,6 +263,30 @@ def forward(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                 _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
                                 _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
                                 lse_p, _ws(workspace), _stream(stream)), "svattn_forward")
+    return out
+
+
+def forward_fused(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  masks: Sequence[Mask], maps: Sequence[TileMap], scales: Sequence[float],
+                  perm: Optional[torch.Tensor], out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Forward over frame-major [heads, N, d] tensors with the temporal-major
+    permutation fused in: heads whose mask order is TEMPORAL_MAJOR are computed
+    in that order through ``perm`` (int32 [N] from permutation_index)."""
+    heads = q.shape[0]
+    out = _qkvo(q, k, v, out, geom.n)
+    if len(masks) != heads or len(maps) != heads:
+        raise SvattnError("need one mask and one map per head")
+    marr = (Mask * heads)(*[Mask(m.kind, m.order, m.window, m.radius) for m in masks])
+    P = ctypes.POINTER(_TileMapC)
+    parr = (P * heads)(*[ctypes.pointer(m.c) for m in maps])
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    perm_p = _dev(perm, "perm", torch.int32) if perm is not None else None
+    _check(lib().svattn_forward_fused(ctypes.byref(geom), heads, q.shape[2], marr, parr, _scales(scales, heads),
+                                      perm_p, _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                                      _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
+                                      lse_p, _ws(workspace), _stream(stream)), "svattn_forward_fused")
     return out
 
 

@@ -113,7 +113,8 @@ hipError_t dispatch_forward(const FwdArgs& a, int head_dim, int bq, int bk, hipS
   if (a.dense_bits)
     return head_dim == 128 ? launch_forward_d128_bits(a, bq, bk, st) : launch_forward_d64_bits(a, bq, bk, st);
   bool all_dense = true;
-  for (int i = 0; i < a.n_slots; ++i) all_dense = all_dense && a.heads[i].kind == SVATTN_DENSE;
+  for (int i = 0; i < a.n_slots; ++i)
+    all_dense = all_dense && a.heads[i].kind == SVATTN_DENSE && !a.heads[i].perm;  // gathered: plain schedule
   return head_dim == 128 ? launch_forward_d128_map(a, bq, bk, all_dense, st)
                          : launch_forward_d64_map(a, bq, bk, all_dense, st);
 }
@@ -324,7 +325,8 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
 
 static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32_t head_dim,
                         const svattn_mask* masks, const svattn_tile_map* const* maps, const float* scales,
-                        const std::vector<HeadPtrs>& ptrs, void* workspace, void* stream) {
+                        const std::vector<HeadPtrs>& ptrs, void* workspace, void* stream,
+                        const int32_t* perm = nullptr) {
   int s;
   if (!masks || !maps) return fail(SVATTN_ERR_INVALID_ARG, "masks / maps is NULL");
   int bq = 0, bk = 0;
@@ -368,6 +370,7 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
     d.col = maps[h]->col;
     d.col_cls = maps[h]->col_cls;
     d.qt_order = maps[h]->qt_order;
+    d.perm = masks[h].order == SVATTN_TEMPORAL_MAJOR ? perm : nullptr;
     d.scale = scales[h];
     d.scale_log2 = scales[h] * kLog2eHost;
     d.kind = masks[h].kind;
@@ -417,6 +420,29 @@ int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim
   std::vector<HeadPtrs> p(heads);
   for (int h = 0; h < heads; ++h) p[h] = HeadPtrs{q[h], k[h], v[h], o[h], lse ? lse[h] : nullptr};
   return forward_impl(geom, n, heads, head_dim, masks, maps, scales, p, workspace, stream);
+}
+
+int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
+                         const svattn_tile_map* const* maps, const float* scales, const int32_t* perm, const void* q,
+                         const void* k, const void* v, void* o, float* lse, void* workspace, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if ((s = check_common(heads, head_dim, scales))) return s;
+  if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
+  if (!masks) return fail(SVATTN_ERR_INVALID_ARG, "masks is NULL");
+  bool any_tm = false;
+  for (int h = 0; h < heads; ++h) any_tm = any_tm || masks[h].order == SVATTN_TEMPORAL_MAJOR;
+  if (any_tm) {
+    if (!perm) return fail(SVATTN_ERR_INVALID_ARG, "perm is NULL but a head runs in temporal-major order");
+    if (!aligned(perm, 4)) return fail(SVATTN_ERR_INVALID_ARG, "perm must be 4-byte aligned");
+    const size_t pb = (size_t)n * 4, ob = (size_t)heads * n * head_dim * 2;
+    if (overlap(perm, pb, o, ob) || (lse && overlap(perm, pb, lse, (size_t)heads * n * 4)) ||
+        (workspace && overlap(perm, pb, workspace, SVATTN_FORWARD_WORKSPACE_BYTES)))
+      return fail(SVATTN_ERR_INVALID_ARG, "perm overlaps an output or the workspace");
+  }
+  return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
+                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream, any_tm ? perm : nullptr);
 }
 
 int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim, const uint32_t* mask_bits,

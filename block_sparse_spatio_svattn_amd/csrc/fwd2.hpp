@@ -138,11 +138,12 @@ __device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
   return below_hi & ~below_lo;
 }
 
-template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST>
+template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST, bool GTH>
 __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   using C = Cfg<D, BK, NW, QG>;
   static_assert(BK % 32 == 0 && (D == 64 || D == 128), "tile shape");
   static_assert(!PP || NW == 8, "the two-group schedule pairs waves w and w + 4 on one SIMD");
+  static_assert(!GTH || (!PP && !BITS), "gathered heads run the plain schedule over tile maps");
   constexpr int STAGES = PP ? 3 : 2;
   __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
@@ -189,8 +190,9 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
     const int qi = min(q0 + gq * 32 + l32, N - 1);
+    const int qr = (GTH && hd.perm) ? hd.perm[qi] : qi;  // gathered head: the row holding position qi
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) qf[gq][ds] = *(const bf16x8*)(Q + (size_t)qi * D + ds * 16 + hh * 8);
+    for (int ds = 0; ds < C::DS; ++ds) qf[gq][ds] = *(const bf16x8*)(Q + (size_t)qr * D + ds * 16 + hh * 8);
   }
   // Wait for Q here: the compiler then knows no load of its own is pending
   // in the loop, where the vector-memory counter belongs to the tile copies.
@@ -316,18 +318,32 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     const bool real = row < BK && slot < C::CPR;
     dma_off[i] = real ? (row * D + (is_k ? slot : (slot ^ vswz<D>(row))) * 8) * 2 : 0;
   }
+  // Gathered heads (hd.perm set): the tensor row holding each lane's key of
+  // every piece, loaded ahead of the copies (a load on the copy's critical
+  // path would stall it).
+  int prow[GTH ? OPC : 1];
+  const bool gathered = GTH && hd.perm != nullptr;
+  auto gather_rows = [&](int key0) __attribute__((always_inline)) {
+    if constexpr (GTH) {
+#pragma unroll
+      for (int i = 0; i < OPC; ++i) prow[i] = hd.perm[min(key0 + dma_off[i] / (D * 2), N - 1)];
+    }
+  };
   // Piece i of this wave for the tile starting at key0, into stage st.
   auto issue_op = [&](int i, int key0, int st) __attribute__((always_inline)) {
     const int o = cw + i * NCW;
     if (cw < 0 || (OPS % NCW != 0 && o >= OPS)) return;
     const bool is_k = o < C::K_PIECES;
-    // The tile's first row as a scalar base address (uniform by construction;
-    // readfirstlane makes that explicit for the asm's SGPR operand).
-    const uint64_t b64 = (uint64_t)((const char*)(is_k ? K : V) + (size_t)key0 * (D * 2));
+    // The tile's first row (or, gathered, the head's first row) as a scalar
+    // base address (uniform by construction; readfirstlane makes that
+    // explicit for the asm's SGPR operand).
+    const uint64_t b64 = (uint64_t)((const char*)(is_k ? K : V) + (gathered ? 0 : (size_t)key0 * (D * 2)));
     const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b64 >> 32)) << 32) |
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
     uint32_t off = (uint32_t)dma_off[i];
-    if (key0 + BK > N) {  // ragged tile: rows past N read row N-1 (their keys are masked)
+    if (gathered) {  // row prow[i] of the tensor, same chunk
+      if constexpr (GTH) off = (uint32_t)(prow[i] * (D * 2) + (dma_off[i] % (D * 2)));
+    } else if (key0 + BK > N) {  // ragged tile: rows past N read row N-1 (their keys are masked)
       const int row = (int)(off / (D * 2));
       off = (uint32_t)((min(key0 + row, N - 1) - key0) * (D * 2) + (off - row * (D * 2)));
     }
@@ -697,13 +713,19 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     // Every wave: S, mask and softmax of tile j, then the copies of tile j+1
     // (into the stage of tile j-1; the wave has no LDS reads in flight here),
     // then P V of tile j and one barrier.
-    if (n > 0) issue(key_c, 0);
+    if (n > 0) {
+      if constexpr (GTH)
+        if (gathered) gather_rows(key_c);
+      issue(key_c, 0);
+    }
     wait_tiles();
     __syncthreads();
     int st = 0;  // stage of tile j
     for (int j = 0; j < n; ++j) {
       int key_nn = 0, cls_nn = 0;
       fetch(j + 2, key_nn, cls_nn);
+      if constexpr (GTH)
+        if (gathered && j + 1 < n) gather_rows(key_n);
       // a wave whose queries keep no key of this tile skips S, softmax and P V
       uint64_t keep[QG];
       const int ms = plan(key_c, cls_c, keep);
@@ -733,10 +755,11 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
   __bf16* __restrict__ O = (__bf16*)hd.o;
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
-    const int qi = q0 + gq * 32 + l32;
+    const int qp = q0 + gq * 32 + l32;
     const float l = sum_xor32(l_run[gq]);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    if (qi < N) {
+    if (qp < N) {
+      const int qi = (GTH && hd.perm) ? hd.perm[qp] : qp;  // gathered head: scatter to the row of position qp
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -763,7 +786,7 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
 
 // Workgroups of this kernel resident on the current device at once (cached
 // per device).
-template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST>
+template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST, bool GTH>
 hipError_t resident_workgroups(int* out) {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -773,7 +796,7 @@ hipError_t resident_workgroups(int* out) {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd2_kernel<D, BK, NW, QG, PP, BITS, PST>, NW * 64, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd2_kernel<D, BK, NW, QG, PP, BITS, PST, GTH>, NW * 64, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -786,23 +809,35 @@ hipError_t resident_workgroups(int* out) {
 
 // Persistent schedule when a queue is given (plain schedule over a tile map
 // only: the two-group schedule serves launches of equal-length rows, where a
-// static grid already balances), else the static grid.
-template <int D, int BK, int NW, int QG, bool PP, bool BITS = false>
-hipError_t launch(const FwdArgs& a, hipStream_t st) {
+// static grid already balances), else the static grid.  Launches with
+// gathered heads use their own instantiation, so the others carry no code for
+// it.
+template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool GTH>
+hipError_t launch_sched(const FwdArgs& a, hipStream_t st) {
   if constexpr (!PP && !BITS) {
     if (a.queue) {
       int resident = 0;
-      hipError_t e = resident_workgroups<D, BK, NW, QG, PP, BITS, true>(&resident);
+      hipError_t e = resident_workgroups<D, BK, NW, QG, PP, BITS, true, GTH>(&resident);
       if (e != hipSuccess) return e;
       const int grid = resident < a.n_items ? resident : a.n_items;
-      hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS, true>), dim3(grid), dim3(NW * 64), 0, st, a);
+      hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS, true, GTH>), dim3(grid), dim3(NW * 64), 0, st, a);
       return hipGetLastError();
     }
   }
   const int per_round = 8 * a.chunk;
   const int grid = ((a.n_items + per_round - 1) / per_round) * per_round;
-  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS, false>), dim3(grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((fwd2_kernel<D, BK, NW, QG, PP, BITS, false, GTH>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
+}
+
+template <int D, int BK, int NW, int QG, bool PP, bool BITS = false>
+hipError_t launch(const FwdArgs& a, hipStream_t st) {
+  if constexpr (!PP && !BITS) {
+    bool gather = false;
+    for (int i = 0; i < a.n_slots; ++i) gather = gather || a.heads[i].perm != nullptr;
+    if (gather) return launch_sched<D, BK, NW, QG, PP, BITS, true>(a, st);
+  }
+  return launch_sched<D, BK, NW, QG, PP, BITS, false>(a, st);
 }
 
 }  // namespace fwd2

@@ -15,7 +15,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import torch
 
 from . import (FRAME_MAJOR, TEMPORAL_MAJOR, Geom, Mask, SvattnError, TileMap, build_tile_map, new_workspace,
-               forward_ptrs, permute_tokens, unpermute)
+               forward_fused, forward_ptrs, permutation_index, permute_tokens, unpermute)
 
 
 def _runs(idx: List[int]) -> List[Tuple[int, int]]:
@@ -31,7 +31,8 @@ def _runs(idx: List[int]) -> List[Tuple[int, int]]:
 
 class SparseVideoAttention:
     def __init__(self, geom: Geom, masks: Sequence[Mask], head_dim: int, block_q: int = 256,
-                 block_k: int = 64, device="cuda", map_flags: int = 0, persistent: bool = True):
+                 block_k: int = 64, device="cuda", map_flags: int = 0, persistent: bool = True,
+                 fused: bool = False):
         self.geom = geom
         self.masks = [Mask(m.kind, m.order, m.window, m.radius) for m in masks]
         self.head_dim = head_dim
@@ -50,6 +51,10 @@ class SparseVideoAttention:
         self._buf = None
         # work counter of the persistent schedule (None: static grid)
         self.workspace = new_workspace(device) if persistent else None
+        # fused: temporal-major heads read and write the frame-major tensors
+        # through the permutation index instead of permuted copies
+        self.fused = fused
+        self.perm = permutation_index(geom, device=device)[0] if fused and self.tm_heads else None
 
     def _buffers(self):
         if self._buf is None:
@@ -96,6 +101,10 @@ class SparseVideoAttention:
         if q.shape != (H, self.geom.n, self.head_dim) or k.shape != q.shape or v.shape != q.shape:
             raise SvattnError(f"expected q/k/v of shape {(H, self.geom.n, self.head_dim)}")
         out = torch.empty_like(q) if out is None else out
+        if self.fused:
+            forward_fused(self.geom, q, k, v, self.masks, self.maps, scales, self.perm, out=out,
+                          workspace=self.workspace, stream=stream)
+            return out
         self.permute_inputs(q, k, v, stream)
         self.attend(q, k, v, out, scales, stream)
         self.unpermute_output(out, stream)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SVATTN_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define SVATTN_VERSION 10200 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 #define SVATTN_OK 0
@@ -205,6 +205,26 @@ SVATTN_API int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32
                                    const float* scales, const void* const* q, const void* const* k,
                                    const void* const* v, void* const* o, float* const* lse,
                                    void* workspace, void* stream);
+
+/*
+ * Forward with the temporal-major permutation fused in: Q, K, V, O (and lse)
+ * of every head stay in frame-major order ([heads, N, head_dim] as for
+ * svattn_forward), and heads whose mask has order TEMPORAL_MAJOR (maps built
+ * for that order) are computed in temporal-major order by reading the rows
+ * of their tensors through perm and writing their O and lse rows back through
+ * it (ainews.tenesys.com, "Co się zmieniło?", item 5, without the separate
+ * reordering passes).  The result equals svattn_permute_tokens, then
+ * svattn_forward, then svattn_unpermute, bit for bit.
+ *   perm  device int32 [N]: perm[t'] = frame-major token at temporal-major
+ *         position t' (svattn_permutation_index); 4-byte aligned; may be NULL
+ *         if no head runs in temporal-major order; must not overlap o, lse or
+ *         the workspace.
+ * Other arguments as for svattn_forward.
+ */
+SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                                    const svattn_mask* masks, const svattn_tile_map* const* maps,
+                                    const float* scales, const int32_t* perm, const void* q, const void* k,
+                                    const void* v, void* o, float* lse, void* workspace, void* stream);
 
 /*
  * Reference forward for an arbitrary mask given as bits (for checking and

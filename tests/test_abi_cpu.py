@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.version() == 10100
+    assert sv.version() == 10200
     L = sv.lib()
     for code, name in [(0, b"SVATTN_OK"), (1, b"SVATTN_ERR_INVALID_ARG"), (2, b"SVATTN_ERR_UNSUPPORTED"),
                        (3, b"SVATTN_ERR_HIP"), (99, b"SVATTN_ERR_UNKNOWN")]:
@@ -213,3 +213,26 @@ def test_traffic_summary_parses():
     t = bench.measured_traffic("headline")
     assert t is None or t == rec["traffic_bytes_per_launch"]
     assert bench.measured_traffic("small") is None
+
+
+def test_forward_fused_validation():
+    L = sv.lib()
+    g = sv.Geom(4, 8, 8)   # N = 256
+    heads, d = 2, 64
+    marr = (sv.Mask * heads)(sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 1), sv.Mask(sv.SPATIAL, 0, 1, 0))
+    m = _map(g, 64, 32)
+    P = ctypes.POINTER(sv._TileMapC)
+    parr = (P * heads)(ctypes.pointer(m), ctypes.pointer(m))
+    sarr = (ctypes.c_float * heads)(0.1, 0.1)
+    q, k, v, o = FAKE, FAKE * 16, FAKE * 32, FAKE * 64
+    f = lambda perm, **kw: L.svattn_forward_fused(ctypes.byref(g), heads, d, marr, parr, sarr, perm, q, k, v,
+                                                  kw.get("o", o), None, kw.get("ws"), None)
+    assert f(None) == INVALID                     # a temporal-major head needs perm
+    assert "perm" in _err()
+    assert f(FAKE * 128 + 2) == INVALID           # misaligned
+    assert f(FAKE * 64 + 1024) == INVALID         # perm inside o
+    assert f(FAKE * 128, ws=FAKE * 128) == INVALID  # perm overlaps the workspace
+    # frame-major heads only: perm may be NULL (fails later only for lack of a device)
+    fm = (sv.Mask * heads)(sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.DENSE, 0, 0, 0))
+    got = L.svattn_forward_fused(ctypes.byref(g), heads, d, fm, parr, sarr, None, q, k, v, o, None, None, None)
+    assert got != INVALID or "perm" not in _err()

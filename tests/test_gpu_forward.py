@@ -345,3 +345,64 @@ def test_tile_aligned_long_runs(sv):
         ref, _ = oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind, head.window,
                                     head.radius, tile_aligned=(head.order, 128, 64))
         assert_close(f64_of(o[h]), ref, f"tile-aligned long runs h{h}")
+
+
+@pytest.mark.parametrize("wl_name,bq,bk,persistent", [("tiny", 256, 64, True), ("tiny", 32, 32, False),
+                                                      ("small", 256, 64, True), ("small", 128, 32, False)])
+def test_fused_permutation_bit_identical(sv, wl_name, bq, bk, persistent):
+    """Temporal-major heads computed straight from the frame-major tensors
+    (rows gathered through the permutation index, O scattered back) give the
+    same bits as permute -> forward -> unpermute."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    wl = synth.WORKLOADS[wl_name]
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    masks = [sv_mask(h) for h in wl.heads]
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    o_sep = SparseVideoAttention(g, masks, wl.head_dim, bq, bk, persistent=persistent)(q, k, v, scales)
+    o_fused = SparseVideoAttention(g, masks, wl.head_dim, bq, bk, persistent=persistent, fused=True)(q, k, v, scales)
+    torch.cuda.synchronize()
+    assert (bits_of(o_sep) == bits_of(o_fused)).all()
+
+
+def test_fused_permutation_lse_and_ragged_long_runs(sv):
+    """lse through the fused entry equals the separate path's lse moved back
+    to frame-major rows; a geometry with 20-frame runs and a ragged tail."""
+    heads = (synth.Head("temporal", radius=1, order="tm"), synth.Head("spatial", window=1),
+             synth.Head("temporal", radius=2, order="tm"), synth.Head("dense", order="tm"))
+    wl = synth.Workload(name="fused", seed=31, frames=21, height=4, width=6, head_dim=128, heads=heads,
+                        tiles=((256, 64),))
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    masks = [sv_mask(h) for h in heads]
+    maps = [sv.build_tile_map(g, m, 256, 64) for m in masks]
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    perm, _ = sv.permutation_index(g)
+    ws = sv.new_workspace()
+    n = wl.n_tokens
+    lse_f = torch.empty(len(heads), n, dtype=torch.float32, device="cuda")
+    o_f = sv.forward_fused(g, q, k, v, masks, maps, scales, perm, lse=lse_f, workspace=ws)
+    # separate path: permuted copies of every temporal-major head
+    tm = [h for h, m in enumerate(masks) if m.order == sv.TEMPORAL_MAJOR]
+    qs, ks, vs = q.clone(), k.clone(), v.clone()
+    for h in tm:
+        for src, dst in ((q, qs), (k, ks), (v, vs)):
+            dst[h:h + 1] = sv.permute_tokens(g, src[h:h + 1])
+    lse_s = torch.empty_like(lse_f)
+    o_s = sv.forward(g, qs, ks, vs, masks, maps, scales, lse=lse_s, workspace=ws)
+    torch.cuda.synchronize()
+    p = perm.long().cpu()
+    o_s, lse_s = o_s.clone(), lse_s.clone()
+    for h in tm:
+        o_s[h] = sv.unpermute(g, o_s[h:h + 1])[0]
+        row = torch.empty_like(lse_s[h].cpu())
+        row[p] = lse_s[h].cpu()
+        lse_s[h] = row.cuda()
+    torch.cuda.synchronize()
+    assert (bits_of(o_f) == bits_of(o_s)).all()
+    assert torch.equal(lse_f, lse_s)
+    ref = _oracle_rows(wl, inp, [np.arange(n)] * len(heads))
+    for h in range(len(heads)):
+        assert_close(f64_of(o_f[h]), ref[h][0], f"fused h{h}")
