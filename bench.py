@@ -81,6 +81,7 @@ def main():
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-aligned", action="store_true", help="skip the tile-aligned traversal")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-permutation step")
+    ap.add_argument("--no-routing", action="store_true", help="skip the head-routing timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -237,6 +238,33 @@ def main():
                                "vs_separate_step": round(ms_step / fused_ms, 3)}
         log(f"step with the permutation fused into the forward {fused_ms:.3f} ms")
         del fused
+
+    # ---- SVG head routing on two sampled q-tiles (excluded from the step, as on the pages) ----
+    if not args.no_routing:
+        sp = next((m for m in masks if m.kind == sv.SPATIAL), sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, 1, 0))
+        tp = next((m for m in masks if m.kind == sv.TEMPORAL), sv.Mask(sv.TEMPORAL, sv.FRAME_MAJOR, 0, 1))
+        sp = sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, sp.window, 0)
+        tp = sv.Mask(sv.TEMPORAL, sv.FRAME_MAJOR, 0, tp.radius)
+        rmaps = [sv.build_tile_map(g, m, args.block_q, args.block_k)
+                 for m in (sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0), sp, tp)]
+        n_full = N // args.block_q
+        qts = [n_full // 3, (2 * n_full) // 3]
+        scratch = torch.empty(sv.route_scratch_bytes(H, D, args.block_q, len(qts)), dtype=torch.uint8, device=q.device)
+        sv.route_heads(g, q, k, v, sp, tp, *rmaps, scales, qts, scratch=scratch)
+        torch.cuda.synchronize()
+        rm = []
+        for _ in range(3):
+            a, b = ev(), ev()
+            a.record(stream)
+            err_r, choice_r = sv.route_heads(g, q, k, v, sp, tp, *rmaps, scales, qts, scratch=scratch)
+            b.record(stream)
+            rm.append((a, b))
+        torch.cuda.synchronize()
+        route_ms = float(np.mean([a.elapsed_time(b) for a, b in rm]))
+        extra["routing"] = {"ms": round(route_ms, 4), "sampled_qtiles": len(qts),
+                            "temporal_heads_chosen": int((choice_r == sv.TEMPORAL).sum().item())}
+        log(f"head routing on {len(qts)} q-tiles per head {route_ms:.3f} ms")
+        del scratch, rmaps
 
     # ---- tile-aligned traversal: every non-empty tile full (a different mask) ----
     if not args.no_aligned:

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR",
     "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "MAP_TILE_ALIGNED", "FORWARD_WORKSPACE_BYTES",
-    "new_workspace", "forward_fused",
+    "new_workspace", "forward_fused", "route_heads", "route_scratch_bytes",
     "SvattnError", "Geom", "Mask", "TileMap", "lib", "version",
     "tile_map_dims", "build_tile_map", "permutation_index", "permute_tokens",
     "unpermute", "forward", "forward_ptrs", "forward_dense_mask",
@@ -101,11 +101,16 @@ def lib() -> ctypes.CDLL:
                                       P(_vp), P(_vp), P(_vp), P(_vp), P(_vp), _vp, _vp]
     L.svattn_forward_fused.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.svattn_route_scratch_bytes.argtypes = [_i32, _i32, _i32, _i32, P(ctypes.c_size_t)]
+    L.svattn_route_heads.argtypes = [P(Geom), _i32, _i32, P(Mask), P(Mask), P(_TileMapC), P(_TileMapC),
+                                     P(_TileMapC), P(ctypes.c_float), P(_i32), _i32, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp, _vp, _vp]
     L.svattn_forward_dense_mask.argtypes = [_i32, _i32, _i32, _vp, _i32, P(ctypes.c_float),
                                             _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     for f in ("svattn_tile_map_dims", "svattn_build_tile_map", "svattn_build_tile_map_ex",
               "svattn_permutation_index", "svattn_permute_tokens", "svattn_unpermute",
-              "svattn_forward", "svattn_forward_ptrs", "svattn_forward_fused", "svattn_forward_dense_mask"):
+              "svattn_forward", "svattn_forward_ptrs", "svattn_forward_fused", "svattn_forward_dense_mask",
+              "svattn_route_scratch_bytes", "svattn_route_heads"):
         getattr(L, f).restype = ctypes.c_int
     _LIB = L
     return L
@@ -288,6 +293,37 @@ def forward_fused(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
                                       lse_p, _ws(workspace), _stream(stream)), "svattn_forward_fused")
     return out
+
+
+def route_scratch_bytes(heads: int, head_dim: int, block_q: int, n_qtiles: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().svattn_route_scratch_bytes(heads, head_dim, block_q, n_qtiles, ctypes.byref(b)),
+           "svattn_route_scratch_bytes")
+    return b.value
+
+
+def route_heads(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, spatial: Mask, temporal: Mask,
+                dense_map: TileMap, spatial_map: TileMap, temporal_map: TileMap, scales: Sequence[float],
+                qtiles: Sequence[int], scratch: Optional[torch.Tensor] = None, stream=None):
+    """SVG head routing over the selected frame-major q-tiles.  Returns
+    (err fp32 [heads, 2] = deviation of the spatial / temporal output from the
+    dense one, choice int32 [heads] = SPATIAL or TEMPORAL), on the device."""
+    heads, d = q.shape[0], q.shape[2]
+    _qkvo(q, k, v, None, geom.n)
+    qt = [int(x) for x in qtiles]
+    need = route_scratch_bytes(heads, d, dense_map.block_q, len(qt))
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=q.device)
+    err = torch.empty(heads, 2, dtype=torch.float32, device=q.device)
+    choice = torch.empty(heads, dtype=torch.int32, device=q.device)
+    _check(lib().svattn_route_heads(ctypes.byref(geom), heads, d, ctypes.byref(spatial), ctypes.byref(temporal),
+                                    ctypes.byref(dense_map.c), ctypes.byref(spatial_map.c),
+                                    ctypes.byref(temporal_map.c), _scales(scales, heads), (_i32 * len(qt))(*qt),
+                                    len(qt), _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                                    _dev(v, "v", torch.bfloat16), _dev(scratch, "scratch"),
+                                    scratch.numel() * scratch.element_size(), _dev(err, "err", torch.float32),
+                                    _dev(choice, "choice", torch.int32), _stream(stream)), "svattn_route_heads")
+    return err, choice
 
 
 def forward_ptrs(geom: Geom, qs: Sequence[torch.Tensor], ks: Sequence[torch.Tensor],

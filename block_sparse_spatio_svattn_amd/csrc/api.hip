@@ -310,7 +310,7 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
     const int nh = (int)std::min<size_t>(kMaxHeadsPerLaunch, descs.size() - h0);
     for (int i = 0; i < nh; ++i) a.heads[i] = descs[h0 + i];
     a.n_slots = nh;
-    a.n_items = nh * a.n_qt;
+    a.n_items = nh * a.n_sel;
     if (a.queue) {
       // launches on one stream run in order, so one counter serves them all
       hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, st, a.queue);
@@ -389,6 +389,7 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
   memset(&a, 0, sizeof(a));
   a.g = make_geo(*geom);
   a.n_qt = (int32_t)cdiv(n, bq);
+  a.n_sel = a.n_qt;
   a.n_kt = (int32_t)cdiv(n, bk);
   a.chunk = 32;
   a.dense_bits = 0;
@@ -445,6 +446,118 @@ int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_di
                       contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream, any_tm ? perm : nullptr);
 }
 
+static int route_dims(int32_t heads, int32_t head_dim, int32_t block_q, int32_t n_qtiles, size_t* part) {
+  if (heads < 1 || heads > (1 << 16)) return fail(SVATTN_ERR_INVALID_ARG, "heads = %d", heads);
+  if (head_dim != 64 && head_dim != 128) return fail(SVATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (!map_bq_ok(block_q)) return fail(SVATTN_ERR_UNSUPPORTED, "block_q %d not in {32, 64, 128, 256}", block_q);
+  if (n_qtiles < 1 || n_qtiles > kMaxSelectedTiles)
+    return fail(SVATTN_ERR_INVALID_ARG, "n_qtiles = %d must be in [1, %d]", n_qtiles, kMaxSelectedTiles);
+  *part = (size_t)heads * n_qtiles * block_q * head_dim * 2;  // one compact output
+  return SVATTN_OK;
+}
+
+int svattn_route_scratch_bytes(int32_t heads, int32_t head_dim, int32_t block_q, int32_t n_qtiles,
+                               size_t* bytes) {
+  size_t part;
+  int s = route_dims(heads, head_dim, block_q, n_qtiles, &part);
+  if (s) return s;
+  if (!bytes) return fail(SVATTN_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 3 * part;
+  return SVATTN_OK;
+}
+
+int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* spatial,
+                       const svattn_mask* temporal, const svattn_tile_map* dense_map,
+                       const svattn_tile_map* spatial_map, const svattn_tile_map* temporal_map, const float* scales,
+                       const int32_t* qtiles, int32_t n_qtiles, const void* q, const void* k, const void* v,
+                       void* scratch, size_t scratch_bytes, float* err, int32_t* choice, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if ((s = check_common(heads, head_dim, scales))) return s;
+  if (!spatial || !temporal) return fail(SVATTN_ERR_INVALID_ARG, "spatial / temporal mask is NULL");
+  if ((s = check_mask(spatial)) || (s = check_mask(temporal))) return s;
+  if (spatial->kind != SVATTN_SPATIAL || temporal->kind != SVATTN_TEMPORAL ||
+      spatial->order != SVATTN_FRAME_MAJOR || temporal->order != SVATTN_FRAME_MAJOR)
+    return fail(SVATTN_ERR_INVALID_ARG, "routing compares a SPATIAL and a TEMPORAL mask, both FRAME_MAJOR");
+  const svattn_tile_map* maps3[3] = {dense_map, spatial_map, temporal_map};
+  for (int m = 0; m < 3; ++m) {
+    const svattn_tile_map* mp = maps3[m];
+    if (!mp || !mp->row_ptr || !mp->col || !mp->col_cls) return fail(SVATTN_ERR_INVALID_ARG, "map %d incomplete", m);
+    if (mp->block_q != dense_map->block_q || mp->block_k != dense_map->block_k)
+      return fail(SVATTN_ERR_INVALID_ARG, "routing maps must share one tile shape");
+    if (!map_bq_ok(mp->block_q) || !fwd_bk_ok(mp->block_k))
+      return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d", mp->block_q, mp->block_k);
+    if (mp->n_qt != cdiv(n, mp->block_q) || mp->n_kt != cdiv(n, mp->block_k))
+      return fail(SVATTN_ERR_INVALID_ARG, "map %d dims do not match the geometry", m);
+    if (!aligned(mp->row_ptr, 4) || !aligned(mp->col, 4) || !aligned(mp->col_cls, 4))
+      return fail(SVATTN_ERR_INVALID_ARG, "map %d: row_ptr, col and col_cls must be 4-byte aligned", m);
+  }
+  const int bq = dense_map->block_q, bk = dense_map->block_k;
+  size_t part;
+  if ((s = route_dims(heads, head_dim, bq, n_qtiles, &part))) return s;
+  if (!qtiles) return fail(SVATTN_ERR_INVALID_ARG, "qtiles is NULL");
+  for (int i = 0; i < n_qtiles; ++i) {
+    if (qtiles[i] < 0 || (int64_t)(qtiles[i] + 1) * bq > n)
+      return fail(SVATTN_ERR_INVALID_ARG, "qtiles[%d] = %d is not a whole q-tile of %lld tokens", i, qtiles[i],
+                  (long long)n);
+    for (int j = 0; j < i; ++j)
+      if (qtiles[j] == qtiles[i]) return fail(SVATTN_ERR_INVALID_ARG, "qtiles[%d] repeats q-tile %d", i, qtiles[i]);
+  }
+  if (!q || !k || !v || !scratch || !err || !choice) return fail(SVATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(scratch, 16) || !aligned(err, 4) ||
+      !aligned(choice, 4))
+    return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / scratch need 16-byte, err / choice 4-byte alignment");
+  if (scratch_bytes < 3 * part)
+    return fail(SVATTN_ERR_INVALID_ARG, "scratch of %zu bytes, %zu needed", scratch_bytes, 3 * part);
+  const size_t tb = (size_t)heads * n * head_dim * 2, eb = (size_t)heads * 8, cb = (size_t)heads * 4;
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins)
+    if (overlap(scratch, 3 * part, in, tb) || overlap(err, eb, in, tb) || overlap(choice, cb, in, tb))
+      return fail(SVATTN_ERR_INVALID_ARG, "scratch / err / choice overlap q, k or v");
+  if (overlap(err, eb, scratch, 3 * part) || overlap(choice, cb, scratch, 3 * part) || overlap(err, eb, choice, cb))
+    return fail(SVATTN_ERR_INVALID_ARG, "scratch, err and choice must not overlap");
+
+  FwdArgs base;
+  memset(&base, 0, sizeof(base));
+  base.g = make_geo(*geom);
+  base.n_qt = (int32_t)cdiv(n, bq);
+  base.n_kt = (int32_t)cdiv(n, bk);
+  base.chunk = 32;
+  base.use_sel = 1;
+  base.compact = 1;
+  base.n_sel = n_qtiles;
+  for (int i = 0; i < n_qtiles; ++i) base.qt_sel[i] = qtiles[i];
+  const svattn_mask dense{SVATTN_DENSE, SVATTN_FRAME_MAJOR, 0, 0};
+  const svattn_mask* masks3[3] = {&dense, spatial, temporal};
+  const size_t hb = (size_t)n * head_dim * 2, ob = (size_t)n_qtiles * bq * head_dim * 2;
+  for (int m = 0; m < 3; ++m) {
+    std::vector<HeadDesc> descs(heads);
+    for (int h = 0; h < heads; ++h) {
+      HeadDesc& d = descs[h];
+      memset(&d, 0, sizeof(d));
+      d.q = (const char*)q + h * hb;
+      d.k = (const char*)k + h * hb;
+      d.v = (const char*)v + h * hb;
+      d.o = (char*)scratch + m * part + h * ob;
+      d.row_ptr = maps3[m]->row_ptr;
+      d.col = maps3[m]->col;
+      d.col_cls = maps3[m]->col_cls;
+      d.scale = scales[h];
+      d.scale_log2 = scales[h] * kLog2eHost;
+      d.kind = masks3[m]->kind;
+      d.order = SVATTN_FRAME_MAJOR;
+      d.window = masks3[m]->window;
+      d.radius = masks3[m]->radius;
+    }
+    if ((s = run_launches(base, descs, head_dim, bq, bk, (hipStream_t)stream))) return s;
+  }
+  hipError_t e = launch_route(scratch, (const char*)scratch + part, (const char*)scratch + 2 * part, heads,
+                              (int64_t)(ob / 2), (int64_t)(ob / 2), err, choice, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "routing launch");
+  return SVATTN_OK;
+}
+
 int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim, const uint32_t* mask_bits,
                               int32_t per_head, const float* scales, const void* q, const void* k, const void* v,
                               void* o, float* lse, int32_t block_q, int32_t block_k, void* stream) {
@@ -483,6 +596,7 @@ int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim,
   svattn_geom g1 = {1, 1, n_tokens};
   a.g = make_geo(g1);
   a.n_qt = (int32_t)cdiv(n, block_q);
+  a.n_sel = a.n_qt;
   a.n_kt = (int32_t)cdiv(n, block_k);
   a.chunk = 32;
   a.dense_bits = 1;

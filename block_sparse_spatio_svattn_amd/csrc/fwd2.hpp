@@ -170,9 +170,10 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     item = __builtin_amdgcn_readfirstlane(ticket);
   }
   while (item < a.n_items) {
-  const int slot = item / a.n_qt;
+  const int slot = item / a.n_sel;
+  const int sel = item - slot * a.n_sel;  // rank of the q-tile among the head's work items
   const HeadDesc& hd = a.heads[slot];
-  const int qt = (BITS || !hd.qt_order) ? item - slot * a.n_qt : ld_const(hd.qt_order + (item - slot * a.n_qt));
+  const int qt = a.use_sel ? a.qt_sel[sel] : (BITS || !hd.qt_order) ? sel : ld_const(hd.qt_order + sel);
   const Geo g = a.g;
   const int N = g.N;
 
@@ -759,7 +760,8 @@ __global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
     const float l = sum_xor32(l_run[gq]);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     if (qp < N) {
-      const int qi = (GTH && hd.perm) ? hd.perm[qp] : qp;  // gathered head: scatter to the row of position qp
+      // gathered head: scatter to the row of position qp; compact output: rank-major rows
+      const int qi = (GTH && hd.perm) ? hd.perm[qp] : a.compact ? sel * C::BQ + (qp - qt * C::BQ) : qp;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll

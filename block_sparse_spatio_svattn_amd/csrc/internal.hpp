@@ -105,6 +105,7 @@ struct HeadDesc {
 
 constexpr int kMaxHeadsPerLaunch = 16;
 constexpr int kMaxDevices = 64;
+constexpr int kMaxSelectedTiles = 32;  // q-tiles of a selected-rows launch (kernel arguments)
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 struct FwdArgs {
@@ -114,11 +115,18 @@ struct FwdArgs {
   int32_t n_slots;        // heads in this launch
   int32_t chunk;          // consecutive work items kept on one XCD (static schedule)
   uint32_t* queue;        // zeroed work counter (persistent schedule), or nullptr
+  int32_t n_sel;          // work items per head: n_qt, or the number of selected q-tiles
+  int32_t use_sel;        // 1: compute only q-tiles qt_sel[0 .. n_sel), the same for every head
+  int32_t compact;        // 1: O / lse rows of selected q-tile i at i * block_q + row (with use_sel)
+  int32_t qt_sel[kMaxSelectedTiles];
   int32_t dense_bits;     // 1: visit every k-tile and mask from bits
   int32_t words_per_row;  // ceil(N/32) for the bit mask
   HeadDesc heads[kMaxHeadsPerLaunch];
 };
 
 hipError_t launch_forward(const FwdArgs& a, int head_dim, int block_q, int block_k, hipStream_t st);
+static_assert(sizeof(FwdArgs) <= 4096, "forward arguments must fit the kernel argument segment");
+hipError_t launch_route(const void* o_dense, const void* o_spatial, const void* o_temporal, int heads,
+                        int64_t per_head, int64_t valid, float* err, int32_t* choice, hipStream_t st);
 
 }  // namespace svattn

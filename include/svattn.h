@@ -34,6 +34,7 @@
 #ifndef SVATTN_H
 #define SVATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__GNUC__) || defined(__clang__)
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SVATTN_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define SVATTN_VERSION 10300 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 #define SVATTN_OK 0
@@ -225,6 +226,40 @@ SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int3
                                     const svattn_mask* masks, const svattn_tile_map* const* maps,
                                     const float* scales, const int32_t* perm, const void* q, const void* k,
                                     const void* v, void* o, float* lse, void* workspace, void* stream);
+
+/*
+ * Head routing (aihirek.info, section "A Sparse VideoGen a figyelmi fejeket
+ * osztályozza", paragraph 3): for a few query rows, each head's dense,
+ * spatial and temporal attention outputs are computed, and the sparse mask
+ * whose output deviates least from the dense one is chosen.  The pages fix
+ * neither the rows nor the deviation; here the rows are the selected whole
+ * q-tiles of the frame-major order (block_q rows each) and the deviation is
+ * the mean squared difference of the bf16 outputs over those rows and all
+ * head_dim columns; a tie goes to the spatial mask.
+ *   spatial, temporal  the two candidate masks, FRAME_MAJOR (window / radius
+ *          as for svattn_forward; the same for every head)
+ *   dense_map, spatial_map, temporal_map  tile maps of the frame-major order
+ *          for a DENSE mask and for spatial / temporal, one tile shape
+ *          (block_q in {32, 64, 128, 256}, block_k in {32, 64})
+ *   scales host fp32 [heads]
+ *   qtiles host int32 [n_qtiles], 1 <= n_qtiles <= 32: distinct q-tiles, each
+ *          wholly inside the sequence ((qtile + 1) * block_q <= N)
+ *   q, k, v frame-major [heads, N, head_dim] bf16 (16-byte aligned)
+ *   scratch device memory of svattn_route_scratch_bytes() bytes (16-byte
+ *          aligned), caller-owned; holds the three outputs of the sampled rows
+ *   err    device fp32 [heads, 2]: deviation of the spatial and the temporal
+ *          output;  choice  device int32 [heads]: SVATTN_SPATIAL or
+ *          SVATTN_TEMPORAL
+ * Scratch, err and choice must not overlap each other or q, k, v.
+ */
+SVATTN_API int svattn_route_scratch_bytes(int32_t heads, int32_t head_dim, int32_t block_q, int32_t n_qtiles,
+                                          size_t* bytes);
+SVATTN_API int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                                  const svattn_mask* spatial, const svattn_mask* temporal,
+                                  const svattn_tile_map* dense_map, const svattn_tile_map* spatial_map,
+                                  const svattn_tile_map* temporal_map, const float* scales, const int32_t* qtiles,
+                                  int32_t n_qtiles, const void* q, const void* k, const void* v, void* scratch,
+                                  size_t scratch_bytes, float* err, int32_t* choice, void* stream);
 
 /*
  * Reference forward for an arbitrary mask given as bits (for checking and

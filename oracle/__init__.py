@@ -53,4 +53,5 @@ from .core import (  # noqa: F401
     attend_rows,
     attend_head,
     unpermute_rows,
+    route_head,
 )

@@ -254,3 +254,24 @@ def unpermute_rows(x_tm: np.ndarray, g: Geometry) -> np.ndarray:
     out = np.empty_like(x_tm)
     out[perm] = x_tm
     return out
+
+
+# ---------------------------------------------------------------------------
+# Head routing (aihirek page, SVG section paragraph 3): for a few queries,
+# the dense, spatial and temporal outputs; the sparse mask whose output
+# deviates least from the dense one is chosen.
+# ---------------------------------------------------------------------------
+
+def route_head(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray, scale: float, g: Geometry,
+               window: int, radius: int, rows: np.ndarray) -> Tuple[float, float, str]:
+    """Deviation of the spatial and temporal outputs from the dense output over
+    frame-major query tokens ``rows``: the mean over rows and columns of the
+    squared difference (the pages name no measure; this is the plain one).
+    Returns (err_spatial, err_temporal, choice), a tie going to "spatial".
+    """
+    od, _ = attend_head(qb, kb, vb, scale, g, "dense", 0, 0, rows=rows)
+    osp, _ = attend_head(qb, kb, vb, scale, g, "spatial", window, 0, rows=rows)
+    ot, _ = attend_head(qb, kb, vb, scale, g, "temporal", 0, radius, rows=rows)
+    es = float(np.mean((osp - od) ** 2))
+    et = float(np.mean((ot - od) ** 2))
+    return es, et, ("temporal" if et < es else "spatial")

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.version() == 10200
+    assert sv.version() == 10300
     L = sv.lib()
     for code, name in [(0, b"SVATTN_OK"), (1, b"SVATTN_ERR_INVALID_ARG"), (2, b"SVATTN_ERR_UNSUPPORTED"),
                        (3, b"SVATTN_ERR_HIP"), (99, b"SVATTN_ERR_UNKNOWN")]:
@@ -236,3 +236,32 @@ def test_forward_fused_validation():
     fm = (sv.Mask * heads)(sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.DENSE, 0, 0, 0))
     got = L.svattn_forward_fused(ctypes.byref(g), heads, d, fm, parr, sarr, None, q, k, v, o, None, None, None)
     assert got != INVALID or "perm" not in _err()
+
+
+def test_route_validation():
+    L = sv.lib()
+    g = sv.Geom(4, 8, 8)   # N = 256, 4 q-tiles of 64
+    heads, d = 2, 64
+    b = ctypes.c_size_t()
+    assert L.svattn_route_scratch_bytes(heads, d, 64, 2, ctypes.byref(b)) == 0
+    assert b.value == 3 * heads * 2 * 64 * d * 2
+    assert L.svattn_route_scratch_bytes(heads, d, 64, 33, ctypes.byref(b)) == INVALID
+    assert L.svattn_route_scratch_bytes(heads, 96, 64, 2, ctypes.byref(b)) == UNSUPPORTED
+    sp, tp = sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.TEMPORAL, 0, 0, 1)
+    m = _map(g, 64, 32)
+    sarr = (ctypes.c_float * heads)(0.1, 0.1)
+    q, k, v, scr, err, ch = FAKE, FAKE * 16, FAKE * 32, FAKE * 64, FAKE * 128, FAKE * 128 + 256
+    def call(qt, spatial=sp, temporal=tp, scratch_bytes=None, **kw):
+        arr = (ctypes.c_int32 * len(qt))(*qt)
+        return L.svattn_route_heads(ctypes.byref(g), heads, d, ctypes.byref(spatial), ctypes.byref(temporal),
+                                    ctypes.byref(m), ctypes.byref(m), ctypes.byref(m), sarr, arr, len(qt), q, k, v,
+                                    kw.get("scr", scr), scratch_bytes if scratch_bytes is not None else b.value,
+                                    kw.get("err", err), ch, None)
+    assert call([0, 4]) == INVALID                  # q-tile 4 is past N
+    assert call([1, 1]) == INVALID                  # repeated
+    assert call([0, 1], spatial=tp) == INVALID      # candidates swapped
+    assert call([0, 1], temporal=sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 1)) == INVALID
+    assert call([0, 1], scratch_bytes=16) == INVALID
+    assert call([0, 1], scr=FAKE * 16 + 64) == INVALID   # scratch inside k
+    assert call([0, 1], err=FAKE * 64 + 32) == INVALID   # err inside scratch
+    assert "overlap" in _err()

@@ -406,3 +406,57 @@ def test_fused_permutation_lse_and_ragged_long_runs(sv):
     ref = _oracle_rows(wl, inp, [np.arange(n)] * len(heads))
     for h in range(len(heads)):
         assert_close(f64_of(o_f[h]), ref[h][0], f"fused h{h}")
+
+
+def _route_setup(sv, wl, window, radius, bq=64, bk=64):
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    sp = sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, window, 0)
+    tp = sv.Mask(sv.TEMPORAL, sv.FRAME_MAJOR, 0, radius)
+    dm = sv.build_tile_map(g, sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0), bq, bk)
+    sm = sv.build_tile_map(g, sp, bq, bk)
+    tm = sv.build_tile_map(g, tp, bq, bk)
+    return g, sp, tp, dm, sm, tm
+
+
+def test_route_heads_closed_forms(sv):
+    """A window covering every frame makes the spatial candidate the dense
+    attention (deviation exactly 0, spatial chosen); a radius covering the
+    grid does the same for the temporal one."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    g, sp, tp, dm, sm, tm = _route_setup(sv, wl, wl.frames, 1)
+    err, ch = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, [3, 40])
+    torch.cuda.synchronize()
+    assert (err[:, 0] == 0).all() and (err[:, 1] > 0).all() and (ch == sv.SPATIAL).all()
+    g, sp, tp, dm, sm, tm = _route_setup(sv, wl, 0, max(wl.height, wl.width))
+    err, ch = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, [0, 7, 74])
+    torch.cuda.synchronize()
+    assert (err[:, 1] == 0).all() and (err[:, 0] > 0).all() and (ch == sv.TEMPORAL).all()
+
+
+@pytest.mark.parametrize("window,radius,bq", [(1, 2, 64), (0, 6, 128), (1, 12, 256)])
+def test_route_heads_against_oracle(sv, window, radius, bq):
+    """Deviations within 5% of the oracle's (fp64 outputs of the same rows);
+    the choice agrees wherever the oracle's two deviations differ by more
+    than 10%."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    g, sp, tp, dm, sm, tm = _route_setup(sv, wl, window, radius, bq=bq)
+    n_qt = wl.n_tokens // bq
+    qtiles = [1, n_qt // 2, n_qt - 2]
+    err, ch = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, qtiles)
+    torch.cuda.synchronize()
+    err, ch = err.cpu().numpy(), ch.cpu().numpy()
+    og = oracle.Geometry(wl.frames, wl.height, wl.width)
+    rows = np.concatenate([np.arange(t * bq, (t + 1) * bq) for t in qtiles])
+    for h in range(wl.n_heads):
+        es, et, choice = oracle.route_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), og, window,
+                                           radius, rows)
+        assert abs(err[h, 0] - es) <= 0.05 * es + 1e-7, (h, err[h], es, et)
+        assert abs(err[h, 1] - et) <= 0.05 * et + 1e-7, (h, err[h], es, et)
+        if abs(es - et) > 0.1 * max(es, et):
+            assert ch[h] == (sv.TEMPORAL if choice == "temporal" else sv.SPATIAL), (h, es, et)

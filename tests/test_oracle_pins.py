@@ -435,3 +435,26 @@ def test_tile_aligned_equals_exact_on_frame_aligned_tiles():
     assert (sp == oracle.keep_matrix(g, "spatial", 1, 0, rows, rows)).all()
     tp = oracle.tile_aligned_keep(g, "temporal", 0, 1, "tm", 32, 32, rows)
     assert tp.sum() > oracle.keep_matrix(g, "temporal", 0, 1, rows, rows).sum()
+
+
+def test_route_head_closed_forms():
+    """Routing pins: a window that covers every frame makes the spatial mask the
+    dense one (zero deviation, spatial chosen); a radius that covers the grid
+    does the same for the temporal mask while the spatial one deviates
+    (temporal chosen); both covering gives a tie (spatial chosen); a constant V
+    gives every mask the same output up to rounding."""
+    g = Geometry(4, 6, 6)
+    wl = synth.Workload(name="route", seed=3, frames=4, height=6, width=6, head_dim=16,
+                        heads=(synth.Head("dense"),), tiles=((32, 32),))
+    inp = synth.make_inputs(wl)
+    q, k, v = inp.q[0], inp.k[0], inp.v[0]
+    rows = np.arange(0, g.n, 5)
+    es, et, ch = oracle.route_head(q, k, v, 0.25, g, 3, 1, rows)
+    assert es == 0.0 and et > 0.0 and ch == "spatial"
+    es, et, ch = oracle.route_head(q, k, v, 0.25, g, 0, 6, rows)
+    assert et == 0.0 and es > 0.0 and ch == "temporal"
+    es, et, ch = oracle.route_head(q, k, v, 0.25, g, 3, 6, rows)
+    assert es == 0.0 and et == 0.0 and ch == "spatial"
+    vc = np.full_like(v, v[0, 0])
+    es, et, _ = oracle.route_head(q, k, vc, 0.25, g, 0, 1, rows)
+    assert es < 1e-28 and et < 1e-28
