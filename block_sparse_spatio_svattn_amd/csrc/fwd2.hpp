@@ -139,7 +139,9 @@ __device__ __forceinline__ uint64_t bit_range(int lo, int hi) {
 }
 
 template <int D, int BK, int NW, int QG, bool PP, bool BITS, bool PST, bool GTH>
-__global__ __launch_bounds__(NW * 64) void fwd2_kernel(const FwdArgs a) {
+// At least two waves per SIMD: workgroups of fewer than eight waves would
+// otherwise be compiled for the whole register file and run one wave per SIMD.
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd2_kernel(const FwdArgs a) {
   using C = Cfg<D, BK, NW, QG>;
   static_assert(BK % 32 == 0 && (D == 64 || D == 128), "tile shape");
   static_assert(!PP || NW == 8, "the two-group schedule pairs waves w and w + 4 on one SIMD");
