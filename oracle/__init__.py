@@ -28,7 +28,8 @@ Readings where the pages are silent (each is listed in the design notes):
   |f_q - f_k| <= w or f_k == 0; temporal keep iff max(|y_q-y_k|, |x_q-x_k|) <= r
   or f_k == 0 (inclusive windows, clipped at grid edges, anchor on the key side);
   temporal-major order is anchor-first: frame 0 in patch order, then for each
-  patch p its frames 1..F-1; tile classes count only in-range pairs; masked
+  patch p its frames 1..F-1 (the library's blocked variant lists the patches
+  4x4 block by block instead of row by row); tile classes count only in-range pairs; masked
   scores are -inf.
 
 Pins (tests/test_oracle_pins.py): closed-form kept counts, the pages' kept
@@ -42,6 +43,9 @@ from .core import (  # noqa: F401
     bf16_to_f64,
     frame_major_coords,
     temporal_major_perm,
+    PATCH_BLOCK,
+    blocked_patch_order,
+    temporal_major_blocked_perm,
     layout_tokens,
     keep_matrix,
     kept_count,

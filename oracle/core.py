@@ -60,12 +60,47 @@ def temporal_major_perm(g: Geometry) -> np.ndarray:
     return np.asarray(order, dtype=np.int64)
 
 
+PATCH_BLOCK = 4
+
+
+def blocked_patch_order(g: Geometry) -> np.ndarray:
+    """Raster patch indices listed in blocked order.
+
+    Not from the pages (they fix only that a temporal head's frames of one
+    patch sit together): the library may also list the patches of a
+    temporal-major layout block by block, so that a run of consecutive
+    positions covers a compact patch region instead of a strip of one patch
+    row.  The grid is cut into PATCH_BLOCK x PATCH_BLOCK blocks (the last block
+    row and column may be smaller), blocks in raster order, patches inside a
+    block in raster order.  Built by sorting the patches on (block row, block
+    column, row in block, column in block), not from a rank formula.
+    """
+    b = PATCH_BLOCK
+    y, x = np.divmod(np.arange(g.patches), g.width)
+    return np.lexsort((x % b, y % b, x // b, y // b)).astype(np.int64)  # last key is the primary one
+
+
+def temporal_major_blocked_perm(g: Geometry) -> np.ndarray:
+    """perm[t'] for the anchor-first temporal-major layout over patches in
+    blocked order: frame 0 in blocked patch order, then for each patch in that
+    order its frames 1..F-1."""
+    seq = blocked_patch_order(g)
+    order = [int(p) for p in seq]
+    for p in seq:
+        for f in range(1, g.frames):
+            order.append(f * g.patches + int(p))
+    return np.asarray(order, dtype=np.int64)
+
+
 def layout_tokens(g: Geometry, order: str) -> np.ndarray:
-    """Frame-major token id held at each position of a head's token order."""
+    """Frame-major token id held at each position of a head's token order
+    ("fm", "tm", or "tmb" for temporal-major over blocked patches)."""
     if order == "fm":
         return np.arange(g.n, dtype=np.int64)
     if order == "tm":
         return temporal_major_perm(g)
+    if order == "tmb":
+        return temporal_major_blocked_perm(g)
     raise ValueError(order)
 
 
@@ -248,9 +283,10 @@ def attend_head(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray, scale: float,
     return o, lse
 
 
-def unpermute_rows(x_tm: np.ndarray, g: Geometry) -> np.ndarray:
-    """Rows stored in temporal-major order -> frame-major order."""
-    perm = temporal_major_perm(g)
+def unpermute_rows(x_tm: np.ndarray, g: Geometry, order: str = "tm") -> np.ndarray:
+    """Rows stored in a head's token order (default temporal-major) ->
+    frame-major order."""
+    perm = layout_tokens(g, order)
     out = np.empty_like(x_tm)
     out[perm] = x_tm
     return out

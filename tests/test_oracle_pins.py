@@ -147,6 +147,40 @@ def test_permutation_hand_examples_and_properties():
         assert (back[perm] == x_tm).all()
 
 
+def test_blocked_patch_order_hand_example_and_properties():
+    ex = _golden("blocked_patch_order.json")
+    H, W = ex["geometry"]["height"], ex["geometry"]["width"]
+    assert oracle.blocked_patch_order(Geometry(1, H, W)).tolist() == ex["order"]
+    tmb = ex["temporal_major_blocked"]
+    perm = oracle.temporal_major_blocked_perm(Geometry(tmb["frames"], H, W))
+    for pos, tok in tmb["pairs"]:
+        assert perm[pos] == tok
+    B = oracle.PATCH_BLOCK
+    for g in (Geometry(4, 8, 8), Geometry(5, 24, 40), Geometry(2, 3, 5), Geometry(1, 4, 4),
+              Geometry(3, 9, 13), Geometry(21, 45, 80)):
+        seq = oracle.blocked_patch_order(g)
+        P = g.patches
+        assert sorted(seq.tolist()) == list(range(P))                  # bijection
+        y, x = seq // g.width, seq % g.width
+        blk = (y // B) * (-(-g.width // B)) + x // B
+        assert (np.diff(blk) >= 0).all()                               # blocks in raster order, each contiguous
+        for b in np.unique(blk):
+            sel = seq[blk == b]
+            assert (np.diff(sel) > 0).all()                            # raster inside the block
+            yy, xx = sel // g.width, sel % g.width
+            assert len(sel) == (np.ptp(yy) + 1) * (np.ptp(xx) + 1) <= B * B   # one whole rectangle
+        perm = oracle.temporal_major_blocked_perm(g)
+        assert sorted(perm.tolist()) == list(range(g.n))
+        assert (perm[:P] == seq).all()                                 # anchor frame in front, blocked order
+        if g.frames > 1:
+            runs = perm[P:].reshape(P, g.frames - 1)                   # one run of frames 1..F-1 per patch
+            f, _, _ = oracle.frame_major_coords(g)
+            assert (f[runs] == np.arange(1, g.frames)[None, :]).all()
+            assert ((runs % P) == seq[:, None]).all()
+        x_l = np.random.default_rng(1).standard_normal((g.n, 2))[perm]
+        assert (oracle.unpermute_rows(x_l, g, "tmb")[perm] == x_l).all()
+
+
 def _inputs(seed, n, d, heads=1):
     q = synth.random_bf16((heads, n, d), seed)
     k = synth.random_bf16((heads, n, d), seed + 1)
@@ -220,19 +254,20 @@ def test_output_inside_kept_value_range():
         assert (o[i] >= kv.min(0) - 1e-12).all() and (o[i] <= kv.max(0) + 1e-12).all()
 
 
-@pytest.mark.parametrize("F,H,W,r", [(4, 8, 8, 1), (5, 6, 10, 2)])
-def test_permute_attend_unpermute_equals_direct(F, H, W, r):
-    """Attention in the temporal-major order, mapped back, equals direct attention."""
+@pytest.mark.parametrize("order", ["tm", "tmb"])
+@pytest.mark.parametrize("F,H,W,r", [(4, 8, 8, 1), (5, 6, 10, 2), (3, 9, 13, 2)])
+def test_permute_attend_unpermute_equals_direct(F, H, W, r, order):
+    """Attention in a temporal-major order, mapped back, equals direct attention."""
     g = Geometry(F, H, W)
     q, k, v = _inputs(60, g.n, 32)
     sc = float(np.float32(0.2))
     direct, dl = oracle.attend_head(q[0], k[0], v[0], sc, g, "temporal", 0, r)
-    perm = oracle.temporal_major_perm(g)
+    perm = oracle.temporal_major_perm(g) if order == "tm" else oracle.temporal_major_blocked_perm(g)
     Q, K, V = (oracle.bf16_to_f64(t[0])[perm] for t in (q, k, v))
     keep_tm = oracle.keep_matrix(g, "temporal", 0, r, perm, perm)
     o_tm, l_tm = oracle.attend_rows(Q, K, V, sc, keep_tm)
-    np.testing.assert_allclose(oracle.unpermute_rows(o_tm, g), direct, rtol=0, atol=1e-13)
-    np.testing.assert_allclose(oracle.unpermute_rows(l_tm[:, None], g)[:, 0], dl, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.unpermute_rows(o_tm, g, order), direct, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.unpermute_rows(l_tm[:, None], g, order)[:, 0], dl, rtol=0, atol=1e-13)
 
 
 # ---------------------------------------------------------------------------
@@ -275,6 +310,17 @@ def _patch_ranges(g, order, a, b):
     return out
 
 
+def _patches_tmb(g, a, b):
+    """(y, x) of the patches covered by positions [a, b) of the blocked
+    temporal-major order (the order itself is pinned above)."""
+    P, F = g.patches, g.frames
+    seq = oracle.blocked_patch_order(g)
+    pos = np.arange(a, b)
+    rank = np.where(pos < P, pos, (pos - P) // max(F - 1, 1))
+    p = np.unique(seq[rank])
+    return p // g.width, p % g.width
+
+
 def _frames(g, order, a, b):
     assert order == "fm"
     return a // g.patches, (b - 1) // g.patches
@@ -293,6 +339,11 @@ def _geometric_class(g, kind, w, r, order, r0, r1, c0, c1):
         c, d = _frames(g, order, n0, c1)
         near_any = max(0, a - d, c - b) <= w
         near_all = max(b - c, d - a) <= w
+    elif order == "tmb":
+        # the rows' and non-frame-0 columns' patches, listed explicitly
+        R, C = _patches_tmb(g, r0, r1), _patches_tmb(g, n0, c1)
+        cheb = np.maximum(np.abs(R[0][:, None] - C[0][None]), np.abs(R[1][:, None] - C[1][None]))
+        near_any, near_all = cheb.min() <= r, cheb.max() <= r
     else:
         R = [x for lo, hi in _patch_ranges(g, order, r0, r1) for x in _rects(lo, hi, g.width)]
         C = [x for lo, hi in _patch_ranges(g, order, n0, c1) for x in _rects(lo, hi, g.width)]
@@ -325,8 +376,12 @@ CASES = [
     (Geometry(4, 8, 8), "dense", 0, 0, "fm", 32, 64),
     (Geometry(3, 5, 7), "temporal", 0, 1, "tm", 32, 32),     # ragged: N = 105
     (Geometry(3, 5, 7), "spatial", 0, 0, "fm", 64, 32),
+    (Geometry(4, 8, 8), "temporal", 0, 1, "tmb", 32, 32),
+    (Geometry(3, 5, 7), "temporal", 0, 1, "tmb", 32, 32),     # ragged blocks and tiles
+    (Geometry(3, 9, 13), "temporal", 0, 2, "tmb", 32, 64),
 ] + [(Geometry(5, 24, 40), kind, w, r, order, bq, bk)
-     for (kind, w, r, order) in [("spatial", 1, 0, "fm"), ("temporal", 0, 2, "fm"), ("temporal", 0, 2, "tm")]
+     for (kind, w, r, order) in [("spatial", 1, 0, "fm"), ("temporal", 0, 2, "fm"), ("temporal", 0, 2, "tm"),
+                                 ("temporal", 0, 2, "tmb")]
      for bq in (64, 128) for bk in (64, 128)]
 
 
@@ -358,7 +413,7 @@ def test_spatial_frame_aligned_tiles_are_never_boundary():
 
 
 @pytest.mark.parametrize("kind,w,r,order", [("spatial", 1, 0, "fm"), ("temporal", 0, 31, "tm"),
-                                            ("temporal", 0, 31, "fm")])
+                                            ("temporal", 0, 31, "fm"), ("temporal", 0, 31, "tmb")])
 def test_headline_tile_rows_match_geometry(kind, w, r, order):
     g = Geometry(21, 45, 80)
     qtiles = [0, 14, 15, 150, 295]
