@@ -15,7 +15,11 @@ Prints one JSON line.  `value` is effective TFLOP/s of the whole step
 `roofline` is for the dominant kernel (the attention forward), timed with
 HIP events on the stream it is launched on.
 
-    python bench.py [--steps K] [--warmup W] [--workload headline]
+    python bench.py [--steps K] [--warmup W] [--workload headline] [--temporal-order tmb|tm|fm]
+
+Temporal heads run by default in the temporal-major order over 4x4 patch
+blocks (the library's layout; the pages' temporal-major order lists patches
+row by row and is timed beside it as `other_temporal_order`).
 """
 from __future__ import annotations
 
@@ -75,13 +79,17 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--block-q", type=int, default=256)
     ap.add_argument("--block-k", type=int, default=64)
-    ap.add_argument("--temporal-order", choices=["tm", "fm"], default="tm")
+    ap.add_argument("--temporal-order", choices=["tm", "tmb", "fm"], default="tmb",
+                    help="token order of the temporal heads: temporal-major (patches in raster order), "
+                         "temporal-major over 4x4 patch blocks, or frame-major")
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-aligned", action="store_true", help="skip the tile-aligned traversal")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-permutation step")
     ap.add_argument("--no-routing", action="store_true", help="skip the head-routing timing")
+    ap.add_argument("--no-alt-order", action="store_true",
+                    help="skip the forward with the temporal heads in the other temporal-major order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -106,8 +114,10 @@ def main():
     kinds = {synth.SPATIAL: sv.SPATIAL, synth.TEMPORAL: sv.TEMPORAL, synth.DENSE: sv.DENSE}
     masks = []
     for h in wl.heads:
-        tm = h.kind == synth.TEMPORAL and args.temporal_order == "tm"
-        masks.append(sv.Mask(kinds[h.kind], sv.TEMPORAL_MAJOR if tm else sv.FRAME_MAJOR, h.window, h.radius))
+        order = sv.FRAME_MAJOR
+        if h.kind == synth.TEMPORAL:
+            order = {"tm": sv.TEMPORAL_MAJOR, "tmb": sv.TEMPORAL_MAJOR_BLOCKED, "fm": sv.FRAME_MAJOR}[args.temporal_order]
+        masks.append(sv.Mask(kinds[h.kind], order, h.window, h.radius))
     H, N, D = wl.n_heads, wl.n_tokens, wl.head_dim
 
     log(f"workload {wl.name}: N={N} heads={H} d={D} tiles {args.block_q}x{args.block_k}")
@@ -179,6 +189,31 @@ def main():
     peak = metrics.BF16_PEAK_TFLOPS
 
     extra = {}
+    # ---- the other temporal-major order (patches in raster order vs 4x4 blocks) ----
+    if not args.no_alt_order and args.temporal_order in ("tm", "tmb"):
+        alt = "tm" if args.temporal_order == "tmb" else "tmb"
+        alt_order = sv.TEMPORAL_MAJOR if alt == "tm" else sv.TEMPORAL_MAJOR_BLOCKED
+        amasks = [sv.Mask(m.kind, alt_order if m.order != sv.FRAME_MAJOR else m.order, m.window, m.radius)
+                  for m in masks]
+        alayer = SparseVideoAttention(g, amasks, D, args.block_q, args.block_k)
+        aout = torch.empty_like(out)
+        alayer.permute_inputs(q, k, v)
+        alayer.attend(q, k, v, aout, scales)
+        torch.cuda.synchronize()
+        am = []
+        for _ in range(args.dense_steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            alayer.attend(q, k, v, aout, scales)
+            b.record(stream)
+            am.append((a, b))
+        torch.cuda.synchronize()
+        alt_ms = float(np.mean([a.elapsed_time(b) for a, b in am]))
+        anz = {str((m.kind, m.order, m.window, m.radius)): mp.nnz() for m, mp in zip(alayer.masks, alayer.maps)}
+        log(f"forward with temporal heads in order {alt}: {alt_ms:.3f} ms; nnz {anz}")
+        extra["other_temporal_order"] = {"order": alt, "ms": round(alt_ms, 4),
+                                         "forward_ms_ratio": round(alt_ms / fwd_ms, 3)}
+        del alayer, aout
     # ---- dense comparator: the same kernel, every tile full ----
     if not args.no_dense:
         dmask = [sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0)] * H

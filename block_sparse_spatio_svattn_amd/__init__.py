@@ -20,7 +20,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR",
+    "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR", "TEMPORAL_MAJOR_BLOCKED", "PATCH_BLOCK",
     "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "MAP_TILE_ALIGNED", "FORWARD_WORKSPACE_BYTES",
     "new_workspace", "forward_fused", "route_heads", "route_scratch_bytes",
     "SvattnError", "Geom", "Mask", "TileMap", "lib", "version",
@@ -29,7 +29,8 @@ __all__ = [
 ]
 
 SPATIAL, TEMPORAL, DENSE = 0, 1, 2
-FRAME_MAJOR, TEMPORAL_MAJOR = 0, 1
+FRAME_MAJOR, TEMPORAL_MAJOR, TEMPORAL_MAJOR_BLOCKED = 0, 1, 2
+PATCH_BLOCK = 4  # SVATTN_PATCH_BLOCK: patches per block side in TEMPORAL_MAJOR_BLOCKED
 TILE_EMPTY, TILE_BOUNDARY, TILE_FULL = 0, 1, 2
 MAP_ALL_BOUNDARY = 1
 MAP_TILE_ALIGNED = 2
@@ -95,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.svattn_permutation_index.argtypes = [P(Geom), _vp, _vp, _vp]
     L.svattn_permute_tokens.argtypes = [P(Geom), _i32, _i32, _vp, _vp, _vp]
     L.svattn_unpermute.argtypes = [P(Geom), _i32, _i32, _vp, _vp, _vp]
+    L.svattn_permutation_index_order.argtypes = [P(Geom), _i32, _vp, _vp, _vp]
+    L.svattn_permute_tokens_order.argtypes = [P(Geom), _i32, _i32, _i32, _vp, _vp, _vp]
+    L.svattn_unpermute_order.argtypes = [P(Geom), _i32, _i32, _i32, _vp, _vp, _vp]
     L.svattn_forward.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.svattn_forward_ptrs.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
@@ -109,6 +113,7 @@ def lib() -> ctypes.CDLL:
                                             _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     for f in ("svattn_tile_map_dims", "svattn_build_tile_map", "svattn_build_tile_map_ex",
               "svattn_permutation_index", "svattn_permute_tokens", "svattn_unpermute",
+              "svattn_permutation_index_order", "svattn_permute_tokens_order", "svattn_unpermute_order",
               "svattn_forward", "svattn_forward_ptrs", "svattn_forward_fused", "svattn_forward_dense_mask",
               "svattn_route_scratch_bytes", "svattn_route_heads"):
         getattr(L, f).restype = ctypes.c_int
@@ -187,33 +192,44 @@ def build_tile_map(geom: Geom, mask: Mask, block_q: int, block_k: int, device="c
     return TileMap(geom, block_q, block_k, device).rebuild(mask, flags, stream)
 
 
-def permutation_index(geom: Geom, device="cuda", stream=None):
+def permutation_index(geom: Geom, device="cuda", stream=None, order: int = TEMPORAL_MAJOR):
+    """perm[t'] = frame-major token at position t' of `order`, and its inverse."""
     perm = torch.empty(geom.n, dtype=torch.int32, device=device)
     inv = torch.empty(geom.n, dtype=torch.int32, device=device)
-    _check(lib().svattn_permutation_index(ctypes.byref(geom), _dev(perm, "perm"), _dev(inv, "inv"),
-                                          _stream(stream)), "svattn_permutation_index")
+    if order == TEMPORAL_MAJOR:
+        st = lib().svattn_permutation_index(ctypes.byref(geom), _dev(perm, "perm"), _dev(inv, "inv"), _stream(stream))
+    else:
+        st = lib().svattn_permutation_index_order(ctypes.byref(geom), order, _dev(perm, "perm"), _dev(inv, "inv"),
+                                                  _stream(stream))
+    _check(st, "svattn_permutation_index")
     return perm, inv
 
 
-def _permute(geom, x, out, stream, fn, what):
+def _permute(geom, x, out, stream, order, to_tm, what):
     if x.dim() != 3 or x.shape[1] != geom.n:
         raise SvattnError(f"{what}: expected [heads, {geom.n}, d], got {tuple(x.shape)}")
     out = torch.empty_like(x) if out is None else out
     if out.shape != x.shape:
         raise SvattnError(f"{what}: out shape {tuple(out.shape)} != {tuple(x.shape)}")
-    _check(fn(ctypes.byref(geom), x.shape[0], x.shape[2], _dev(x, "src", torch.bfloat16),
-              _dev(out, "dst", torch.bfloat16), _stream(stream)), what)
+    args = (x.shape[0], x.shape[2], _dev(x, "src", torch.bfloat16), _dev(out, "dst", torch.bfloat16), _stream(stream))
+    L = lib()
+    if order == TEMPORAL_MAJOR:
+        st = (L.svattn_permute_tokens if to_tm else L.svattn_unpermute)(ctypes.byref(geom), *args)
+    else:
+        st = (L.svattn_permute_tokens_order if to_tm else L.svattn_unpermute_order)(ctypes.byref(geom), order, *args)
+    _check(st, what)
     return out
 
 
-def permute_tokens(geom: Geom, x: torch.Tensor, out=None, stream=None) -> torch.Tensor:
-    """Frame-major -> anchor-first temporal-major rows of a [heads, N, d] bf16 tensor."""
-    return _permute(geom, x, out, stream, lib().svattn_permute_tokens, "svattn_permute_tokens")
+def permute_tokens(geom: Geom, x: torch.Tensor, out=None, stream=None, order: int = TEMPORAL_MAJOR) -> torch.Tensor:
+    """Frame-major -> temporal-major rows (anchor-first; `order` TEMPORAL_MAJOR
+    or TEMPORAL_MAJOR_BLOCKED) of a [heads, N, d] bf16 tensor."""
+    return _permute(geom, x, out, stream, order, True, "svattn_permute_tokens")
 
 
-def unpermute(geom: Geom, x: torch.Tensor, out=None, stream=None) -> torch.Tensor:
-    """Temporal-major -> frame-major rows of a [heads, N, d] bf16 tensor."""
-    return _permute(geom, x, out, stream, lib().svattn_unpermute, "svattn_unpermute")
+def unpermute(geom: Geom, x: torch.Tensor, out=None, stream=None, order: int = TEMPORAL_MAJOR) -> torch.Tensor:
+    """Temporal-major (`order`) -> frame-major rows of a [heads, N, d] bf16 tensor."""
+    return _permute(geom, x, out, stream, order, False, "svattn_unpermute")
 
 
 def _qkvo(q, k, v, out, n):

@@ -55,8 +55,10 @@ int check_mask(const svattn_mask* m) {
   if (!m) return fail(SVATTN_ERR_INVALID_ARG, "mask is NULL");
   if (m->kind < SVATTN_SPATIAL || m->kind > SVATTN_DENSE)
     return fail(SVATTN_ERR_INVALID_ARG, "mask kind %d is not SPATIAL/TEMPORAL/DENSE", m->kind);
-  if (m->order != SVATTN_FRAME_MAJOR && m->order != SVATTN_TEMPORAL_MAJOR)
-    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not FRAME_MAJOR/TEMPORAL_MAJOR", m->order);
+  if (m->order != SVATTN_FRAME_MAJOR && m->order != SVATTN_TEMPORAL_MAJOR &&
+      m->order != SVATTN_TEMPORAL_MAJOR_BLOCKED)
+    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not FRAME_MAJOR/TEMPORAL_MAJOR/TEMPORAL_MAJOR_BLOCKED",
+                m->order);
   if (m->window < 0 || m->radius < 0)
     return fail(SVATTN_ERR_INVALID_ARG, "window %d / radius %d must be >= 0", m->window, m->radius);
   if (m->kind == SVATTN_SPATIAL && m->order != SVATTN_FRAME_MAJOR)
@@ -185,23 +187,33 @@ int svattn_build_tile_map(const svattn_geom* geom, const svattn_mask* mask, svat
 }
 
 int svattn_permutation_index(const svattn_geom* geom, int32_t* perm, int32_t* inv, void* stream) {
+  return svattn_permutation_index_order(geom, SVATTN_TEMPORAL_MAJOR, perm, inv, stream);
+}
+
+int svattn_permutation_index_order(const svattn_geom* geom, int32_t order, int32_t* perm, int32_t* inv,
+                                   void* stream) {
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
+  if (order != SVATTN_FRAME_MAJOR && order != SVATTN_TEMPORAL_MAJOR && order != SVATTN_TEMPORAL_MAJOR_BLOCKED)
+    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not FRAME_MAJOR / TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED",
+                order);
   if (!perm) return fail(SVATTN_ERR_INVALID_ARG, "perm is NULL");
   if (!aligned(perm, 4) || (inv && !aligned(inv, 4)))
     return fail(SVATTN_ERR_INVALID_ARG, "perm / inv must be 4-byte aligned");
   if (inv && overlap(perm, n * 4, inv, n * 4)) return fail(SVATTN_ERR_INVALID_ARG, "perm and inv overlap");
-  hipError_t e = launch_perm_index(make_geo(*geom), perm, inv, (hipStream_t)stream);
+  hipError_t e = launch_perm_index(make_geo(*geom), order, perm, inv, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "permutation index launch");
   return SVATTN_OK;
 }
 
-static int permute_common(const svattn_geom* geom, int32_t heads, int32_t head_dim, const void* src, void* dst,
-                          bool to_tm, void* stream) {
+static int permute_common(const svattn_geom* geom, int32_t order, int32_t heads, int32_t head_dim,
+                          const void* src, void* dst, bool to_tm, void* stream) {
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
+  if (order != SVATTN_TEMPORAL_MAJOR && order != SVATTN_TEMPORAL_MAJOR_BLOCKED)
+    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED", order);
   if (heads < 1) return fail(SVATTN_ERR_INVALID_ARG, "heads = %d must be >= 1", heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(SVATTN_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);
@@ -211,19 +223,29 @@ static int permute_common(const svattn_geom* geom, int32_t heads, int32_t head_d
   if (chunks >= (1ll << 31)) return fail(SVATTN_ERR_UNSUPPORTED, "tensor too large (%lld rows)", (long long)(heads * n));
   const size_t bytes = (size_t)heads * n * head_dim * 2;
   if (overlap(src, bytes, dst, bytes)) return fail(SVATTN_ERR_INVALID_ARG, "src and dst overlap (no in-place)");
-  hipError_t e = launch_permute(make_geo(*geom), heads, head_dim, src, dst, to_tm, (hipStream_t)stream);
+  hipError_t e = launch_permute(make_geo(*geom), order, heads, head_dim, src, dst, to_tm, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   return SVATTN_OK;
 }
 
 int svattn_permute_tokens(const svattn_geom* geom, int32_t heads, int32_t head_dim, const void* src, void* dst,
                           void* stream) {
-  return permute_common(geom, heads, head_dim, src, dst, true, stream);
+  return permute_common(geom, SVATTN_TEMPORAL_MAJOR, heads, head_dim, src, dst, true, stream);
 }
 
 int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t head_dim, const void* src, void* dst,
                      void* stream) {
-  return permute_common(geom, heads, head_dim, src, dst, false, stream);
+  return permute_common(geom, SVATTN_TEMPORAL_MAJOR, heads, head_dim, src, dst, false, stream);
+}
+
+int svattn_permute_tokens_order(const svattn_geom* geom, int32_t order, int32_t heads, int32_t head_dim,
+                                const void* src, void* dst, void* stream) {
+  return permute_common(geom, order, heads, head_dim, src, dst, true, stream);
+}
+
+int svattn_unpermute_order(const svattn_geom* geom, int32_t order, int32_t heads, int32_t head_dim,
+                           const void* src, void* dst, void* stream) {
+  return permute_common(geom, order, heads, head_dim, src, dst, false, stream);
 }
 
 static int check_common(int32_t heads, int32_t head_dim, const float* scales) {
@@ -370,7 +392,7 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
     d.col = maps[h]->col;
     d.col_cls = maps[h]->col_cls;
     d.qt_order = maps[h]->qt_order;
-    d.perm = masks[h].order == SVATTN_TEMPORAL_MAJOR ? perm : nullptr;
+    d.perm = masks[h].order != SVATTN_FRAME_MAJOR ? perm : nullptr;
     d.scale = scales[h];
     d.scale_log2 = scales[h] * kLog2eHost;
     d.kind = masks[h].kind;
@@ -432,8 +454,14 @@ int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_di
   if ((s = check_common(heads, head_dim, scales))) return s;
   if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
   if (!masks) return fail(SVATTN_ERR_INVALID_ARG, "masks is NULL");
-  bool any_tm = false;
-  for (int h = 0; h < heads; ++h) any_tm = any_tm || masks[h].order == SVATTN_TEMPORAL_MAJOR;
+  bool any_tm = false, any_tmb = false;
+  for (int h = 0; h < heads; ++h) {
+    any_tm = any_tm || masks[h].order == SVATTN_TEMPORAL_MAJOR;
+    any_tmb = any_tmb || masks[h].order == SVATTN_TEMPORAL_MAJOR_BLOCKED;
+  }
+  if (any_tm && any_tmb)
+    return fail(SVATTN_ERR_INVALID_ARG, "one perm serves one temporal-major order: the call mixes both");
+  any_tm = any_tm || any_tmb;
   if (any_tm) {
     if (!perm) return fail(SVATTN_ERR_INVALID_ARG, "perm is NULL but a head runs in temporal-major order");
     if (!aligned(perm, 4)) return fail(SVATTN_ERR_INVALID_ARG, "perm must be 4-byte aligned");

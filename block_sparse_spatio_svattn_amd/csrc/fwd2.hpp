@@ -247,11 +247,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     l_run[gq] = 0.f;
   }
   const float c = hd.scale_log2;
-  // Keys of a tile fall into runs that share a patch (temporal heads,
-  // temporal-major: runs of F-1 keys) or a patch row (temporal heads,
+  // Keys of a tile fall into runs that share a patch (temporal heads, either
+  // temporal-major order: runs of F-1 keys) or a patch row (temporal heads,
   // frame-major: runs of W keys); a lane decides a whole run at once when runs
   // are at least 16 keys long, else it reads per-key coordinates from LDS.
-  const bool runs_ok = order == SVATTN_TEMPORAL_MAJOR ? g.F - 1 >= 16 : g.W >= 16;
+  const bool runs_ok = order != SVATTN_FRAME_MAJOR ? g.F - 1 >= 16 : g.W >= 16;
   const bool need_kc = kind == SVATTN_TEMPORAL && !runs_ok;
 
   // Tile list: the map's CSR row; with a bit mask, every k-tile.
@@ -454,14 +454,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int s0 = max(key0, g.P) - key0;  // first non-anchor key of the tile
         const int e0 = min(BK, lim_n);         // past the last key of the tile
         if (s0 < e0) {
-          if (order == SVATTN_TEMPORAL_MAJOR) {
-            // run: the F-1 frames of one patch
+          if (order != SVATTN_FRAME_MAJOR) {
+            // run: the F-1 frames of one patch (p: the patch's rank in the
+            // order's patch sequence)
             const int F1 = g.F - 1;
             int p = (int)g.divF1.div((uint32_t)(s0 + key0 - g.P));
             int rs = s0, re = g.P + (p + 1) * F1 - key0;
 #pragma unroll
             for (int i = 0; i < MAXR; ++i) {
-              const int y = (int)g.divW.div((uint32_t)p), x = p - y * g.W;
+              int y, x;
+              if (order == SVATTN_TEMPORAL_MAJOR_BLOCKED) {
+                blocked_yx(g, min(p, g.P - 1), y, x);  // runs past the last patch hold no key
+              } else {
+                y = (int)g.divW.div((uint32_t)p);
+                x = p - y * g.W;
+              }
               const uint64_t rb = bit_range(rs, min(re, e0));
 #pragma unroll
               for (int gq = 0; gq < QG; ++gq) {

@@ -39,7 +39,14 @@ struct FastDiv {
 struct Geo {
   int32_t F, H, W, P, N;
   FastDiv divP, divW, divF1;  // by P, W and max(F-1, 1)
+  // Blocked patch order (B = SVATTN_PATCH_BLOCK): NBR x NBC blocks; the last
+  // block row has HL rows, the last block column WL columns.
+  int32_t NBR, NBC, HL, WL;
+  FastDiv divBW, divBHL, divWL;  // by B*W, B*HL and WL
 };
+
+constexpr int kPatchBlock = SVATTN_PATCH_BLOCK;
+static_assert(kPatchBlock == 4, "block arithmetic below uses shifts by 2 and 4");
 
 inline Geo make_geo(const svattn_geom& g) {
   Geo o;
@@ -51,38 +58,89 @@ inline Geo make_geo(const svattn_geom& g) {
   o.divP = FastDiv((uint32_t)o.P);
   o.divW = FastDiv((uint32_t)o.W);
   o.divF1 = FastDiv((uint32_t)(o.F > 1 ? o.F - 1 : 1));
+  o.NBR = (o.H + kPatchBlock - 1) / kPatchBlock;
+  o.NBC = (o.W + kPatchBlock - 1) / kPatchBlock;
+  o.HL = o.H - (o.NBR - 1) * kPatchBlock;
+  o.WL = o.W - (o.NBC - 1) * kPatchBlock;
+  o.divBW = FastDiv((uint32_t)(kPatchBlock * o.W));
+  o.divBHL = FastDiv((uint32_t)(kPatchBlock * o.HL));
+  o.divWL = FastDiv((uint32_t)o.WL);
   return o;
 }
 
-// Patch index of a token position in a given order (frame-major or
-// anchor-first temporal-major).
-__device__ __forceinline__ int patch_of(const Geo& g, int order, int t) {
-  if (order == SVATTN_FRAME_MAJOR) return (int)g.divP.mod((uint32_t)t);
+// Patch row and column of the patch with rank r in the blocked order: block
+// row tr holds ranks [tr*B*W, (tr+1)*B*W); inside it, block column tc holds
+// B*h ranks (h = B, or HL in the last block row), listed row by row with w =
+// B columns (WL in the last block column).
+__host__ __device__ __forceinline__ void blocked_yx(const Geo& g, int r, int& y, int& x) {
+  const uint32_t tr = g.divBW.div((uint32_t)r);
+  const uint32_t rem = (uint32_t)r - tr * (uint32_t)(kPatchBlock * g.W);
+  const bool last_r = (int)tr == g.NBR - 1;
+  const uint32_t tc = last_r ? g.divBHL.div(rem) : rem >> 4;
+  const uint32_t rem2 = rem - tc * (last_r ? (uint32_t)(kPatchBlock * g.HL) : 16u);
+  const bool last_c = (int)tc == g.NBC - 1;
+  const uint32_t iy = last_c ? g.divWL.div(rem2) : rem2 >> 2;
+  const uint32_t ix = rem2 - iy * (last_c ? (uint32_t)g.WL : 4u);
+  y = (int)(tr * kPatchBlock + iy);
+  x = (int)(tc * kPatchBlock + ix);
+}
+
+// Raster patch index of rank r in the blocked order.
+__host__ __device__ __forceinline__ int blocked_patch(const Geo& g, int r) {
+  int y, x;
+  blocked_yx(g, r, y, x);
+  return y * g.W + x;
+}
+
+// Rank in the blocked order of raster patch p.
+__host__ __device__ __forceinline__ int blocked_rank(const Geo& g, int p) {
+  const int y = (int)g.divW.div((uint32_t)p), x = p - y * g.W;
+  const int tr = y >> 2, tc = x >> 2;
+  const int h = tr == g.NBR - 1 ? g.HL : kPatchBlock;
+  const int w = tc == g.NBC - 1 ? g.WL : kPatchBlock;
+  return tr * kPatchBlock * g.W + tc * kPatchBlock * h + (y - tr * kPatchBlock) * w + (x - tc * kPatchBlock);
+}
+
+// Rank (in the order's patch sequence) of the patch at position t of a
+// temporal-major order.
+__host__ __device__ __forceinline__ int tm_rank(const Geo& g, int t) {
   return t < g.P ? t : (int)g.divF1.div((uint32_t)(t - g.P));
 }
 
-// Frame-major token stored at temporal-major position tp (perm[tp]).
-__host__ __device__ __forceinline__ int tm_to_fm(const Geo& g, int tp) {
-  if (tp < g.P) return tp;
-  uint32_t u = (uint32_t)(tp - g.P);
-  uint32_t p = g.divF1.div(u);
-  uint32_t f = 1 + (u - p * g.divF1.d);
+// Patch index of a token position in a given order (frame-major, or one of
+// the two anchor-first temporal-major orders).
+__host__ __device__ __forceinline__ int patch_of(const Geo& g, int order, int t) {
+  if (order == SVATTN_FRAME_MAJOR) return (int)g.divP.mod((uint32_t)t);
+  const int r = tm_rank(g, t);
+  return order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? blocked_patch(g, r) : r;
+}
+
+// Frame-major token stored at position tp of a temporal-major order (perm[tp]).
+__host__ __device__ __forceinline__ int tm_to_fm(const Geo& g, int order, int tp) {
+  uint32_t f = 0, r = (uint32_t)tp;
+  if (tp >= g.P) {
+    const uint32_t u = (uint32_t)(tp - g.P);
+    r = g.divF1.div(u);
+    f = 1 + (u - r * g.divF1.d);
+  }
+  const uint32_t p = order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? (uint32_t)blocked_patch(g, (int)r) : r;
   return (int)(f * (uint32_t)g.P + p);
 }
 
-// Temporal-major position of frame-major token t (inv[t]).
-__host__ __device__ __forceinline__ int fm_to_tm(const Geo& g, int t) {
-  uint32_t f = g.divP.div((uint32_t)t);
-  uint32_t p = (uint32_t)t - f * (uint32_t)g.P;
-  if (f == 0) return (int)p;
-  return (int)((uint32_t)g.P + p * (uint32_t)(g.F - 1) + (f - 1));
+// Position in a temporal-major order of frame-major token t (inv[t]).
+__host__ __device__ __forceinline__ int fm_to_tm(const Geo& g, int order, int t) {
+  const uint32_t f = g.divP.div((uint32_t)t);
+  const uint32_t p = (uint32_t)t - f * (uint32_t)g.P;
+  const uint32_t r = order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? (uint32_t)blocked_rank(g, (int)p) : p;
+  if (f == 0) return (int)r;
+  return (int)((uint32_t)g.P + r * (uint32_t)(g.F - 1) + (f - 1));
 }
 
 // ---- launchers (defined in the .hip files; return hipError_t) ----
 hipError_t launch_tile_map(const Geo& g, const svattn_mask& m, const svattn_tile_map& map,
                            uint32_t flags, hipStream_t st);
-hipError_t launch_perm_index(const Geo& g, int32_t* perm, int32_t* inv, hipStream_t st);
-hipError_t launch_permute(const Geo& g, int heads, int head_dim, const void* src, void* dst,
+hipError_t launch_perm_index(const Geo& g, int order, int32_t* perm, int32_t* inv, hipStream_t st);
+hipError_t launch_permute(const Geo& g, int order, int heads, int head_dim, const void* src, void* dst,
                           bool to_temporal_major, hipStream_t st);
 
 // Forward: per-head descriptor passed by value in the kernel arguments.

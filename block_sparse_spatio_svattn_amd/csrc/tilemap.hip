@@ -9,12 +9,16 @@
 //
 // Classes are exact and computed from coordinates, one thread per block, with
 // no per-pair work: the rows of a block cover a set of patches that is the
-// union of at most two contiguous patch-index ranges (a frame-major range can
-// wrap once around a frame boundary; an anchor-first temporal-major range can
-// straddle the frame-0 prefix), and each range is at most three grid
-// rectangles.  Between two rectangles the smallest Chebyshev distance is
-// max(gap_y, gap_x) and the largest is max(span_y, span_x).  Key positions
-// below P (frame 0, the anchor) are kept for every query in both orders.
+// union of at most two contiguous ranges of the order's patch sequence (a
+// frame-major range can wrap once around a frame boundary; an anchor-first
+// temporal-major range can straddle the frame-0 prefix).  A range of raster
+// patch indices is at most three grid rectangles, a range of the blocked
+// patch order at most seven (the tail of its first block, whole blocks to the
+// end of that block row, whole block rows, whole blocks from the start of the
+// last block row, the head of its last block).  Between two rectangles the
+// smallest Chebyshev distance is max(gap_y, gap_x) and the largest is
+// max(span_y, span_x).  Key positions below P (frame 0, the anchor) are kept
+// for every query in every order.
 
 #include "internal.hpp"
 
@@ -26,7 +30,7 @@ struct Rect {
 };
 
 // Contiguous patch-index ranges [lo, hi] covered by positions [a, b), b > a.
-__device__ int patch_ranges(const Geo& g, int order, int a, int b, int2 out[2]) {
+__host__ __device__ int patch_ranges(const Geo& g, int order, int a, int b, int2 out[2]) {
   if (order == SVATTN_FRAME_MAJOR) {
     if (b - a >= g.P) {
       out[0] = make_int2(0, g.P - 1);
@@ -51,7 +55,7 @@ __device__ int patch_ranges(const Geo& g, int order, int a, int b, int2 out[2]) 
   return n;
 }
 
-__device__ int rects_of(const Geo& g, int2 r, Rect* out) {
+__host__ __device__ int rects_of(const Geo& g, int2 r, Rect* out) {
   int ylo = (int)g.divW.div((uint32_t)r.x), yhi = (int)g.divW.div((uint32_t)r.y);
   int xlo = r.x - ylo * g.W, xhi = r.y - yhi * g.W;
   if (ylo == yhi) {
@@ -67,16 +71,72 @@ __device__ int rects_of(const Geo& g, int2 r, Rect* out) {
   return 2;
 }
 
-__device__ int rect_set(const Geo& g, int order, int a, int b, Rect out[6]) {
+// Position of rank r of the blocked patch order: block (tr, tc) of h x w
+// patches, index i = row * w + column inside it.
+struct BlockPos {
+  int tr, tc, h, w, i;
+};
+__host__ __device__ BlockPos block_pos(const Geo& g, int r) {
+  int y, x;
+  blocked_yx(g, r, y, x);
+  BlockPos b;
+  b.tr = y / kPatchBlock;
+  b.tc = x / kPatchBlock;
+  b.h = b.tr == g.NBR - 1 ? g.HL : kPatchBlock;
+  b.w = b.tc == g.NBC - 1 ? g.WL : kPatchBlock;
+  b.i = (y - b.tr * kPatchBlock) * b.w + (x - b.tc * kPatchBlock);
+  return b;
+}
+
+// Rectangles of in-block indices [i0, i1] of block b (raster inside the block).
+__host__ __device__ int block_part(const BlockPos& b, int i0, int i1, Rect* out) {
+  const int y0 = b.tr * kPatchBlock, x0 = b.tc * kPatchBlock;
+  const int ya = i0 / b.w, xa = i0 - ya * b.w, yb = i1 / b.w, xb = i1 - yb * b.w;
+  if (ya == yb) {
+    out[0] = Rect{y0 + ya, y0 + ya, x0 + xa, x0 + xb};
+    return 1;
+  }
+  int n = 0;
+  out[n++] = Rect{y0 + ya, y0 + ya, x0 + xa, x0 + b.w - 1};
+  out[n++] = Rect{y0 + yb, y0 + yb, x0, x0 + xb};
+  if (yb > ya + 1) out[n++] = Rect{y0 + ya + 1, y0 + yb - 1, x0, x0 + b.w - 1};
+  return n;
+}
+
+// Rectangles of ranks [r.x, r.y] of the blocked patch order.
+__host__ __device__ int blocked_rects(const Geo& g, int2 r, Rect* out) {
+  const BlockPos a = block_pos(g, r.x), b = block_pos(g, r.y);
+  if (a.tr == b.tr && a.tc == b.tc) return block_part(a, a.i, b.i, out);
+  int n = 0;
+  n += block_part(a, a.i, a.h * a.w - 1, out + n);  // tail of the first block
+  n += block_part(b, 0, b.i, out + n);              // head of the last block
+  if (a.tr == b.tr) {
+    if (b.tc > a.tc + 1)
+      out[n++] = Rect{a.tr * kPatchBlock, a.tr * kPatchBlock + a.h - 1, (a.tc + 1) * kPatchBlock, b.tc * kPatchBlock - 1};
+    return n;
+  }
+  if (a.tc + 1 < g.NBC)  // rest of the first block row
+    out[n++] = Rect{a.tr * kPatchBlock, a.tr * kPatchBlock + a.h - 1, (a.tc + 1) * kPatchBlock, g.W - 1};
+  if (b.tr > a.tr + 1)  // whole block rows between
+    out[n++] = Rect{(a.tr + 1) * kPatchBlock, b.tr * kPatchBlock - 1, 0, g.W - 1};
+  if (b.tc > 0)  // start of the last block row
+    out[n++] = Rect{b.tr * kPatchBlock, b.tr * kPatchBlock + b.h - 1, 0, b.tc * kPatchBlock - 1};
+  return n;
+}
+
+constexpr int kMaxRects = 2 * 9;  // two ranges of at most 3 + 3 + 3 rectangles
+
+__host__ __device__ int rect_set(const Geo& g, int order, int a, int b, Rect out[kMaxRects]) {
   int2 rg[2];
   int nr = patch_ranges(g, order, a, b, rg);
   int n = 0;
-  for (int i = 0; i < nr; ++i) n += rects_of(g, rg[i], out + n);
+  for (int i = 0; i < nr; ++i)
+    n += order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? blocked_rects(g, rg[i], out + n) : rects_of(g, rg[i], out + n);
   return n;
 }
 
 // Class of the block rows [r0, r1) x columns [c0, c1) (both clipped to N).
-__device__ uint8_t classify(const Geo& g, const svattn_mask& m, int r0, int r1, int c0, int c1) {
+__host__ __device__ uint8_t classify(const Geo& g, const svattn_mask& m, int r0, int r1, int c0, int c1) {
   const bool anchor = c0 < g.P;  // some key of the block is in frame 0
   const int n0 = max(c0, g.P);   // first key outside frame 0
   if (n0 >= c1 || m.kind == SVATTN_DENSE) return SVATTN_TILE_FULL;
@@ -87,7 +147,7 @@ __device__ uint8_t classify(const Geo& g, const svattn_mask& m, int r0, int r1, 
     near_any = max(0, max(a - d, c - b)) <= m.window;
     near_all = max(b - c, d - a) <= m.window;
   } else {
-    Rect R[6], C[6];
+    Rect R[kMaxRects], C[kMaxRects];
     int nr = rect_set(g, m.order, r0, r1, R);
     int nc = rect_set(g, m.order, n0, c1, C);
     int dmin = 1 << 30, dmax = 0;

@@ -14,15 +14,15 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (FRAME_MAJOR, TEMPORAL_MAJOR, Geom, Mask, SvattnError, TileMap, build_tile_map, new_workspace,
-               forward_fused, forward_ptrs, permutation_index, permute_tokens, unpermute)
+from . import (FRAME_MAJOR, Geom, Mask, SvattnError, TileMap, build_tile_map, new_workspace, forward_fused,
+               forward_ptrs, permutation_index, permute_tokens, unpermute)
 
 
-def _runs(idx: List[int]) -> List[Tuple[int, int]]:
-    """Maximal runs [a, b) of consecutive integers in a sorted list."""
+def _runs(idx: List[int], key=lambda h: 0) -> List[Tuple[int, int]]:
+    """Maximal runs [a, b) of consecutive integers of a sorted list that share key(h)."""
     out = []
     for h in idx:
-        if out and out[-1][1] == h:
+        if out and out[-1][1] == h and key(h) == key(out[-1][0]):
             out[-1] = (out[-1][0], h + 1)
         else:
             out.append((h, h + 1))
@@ -45,8 +45,9 @@ class SparseVideoAttention:
             if key not in cache:
                 cache[key] = build_tile_map(geom, m, block_q, block_k, device=device, flags=map_flags)
             self.maps.append(cache[key])
-        self.tm_heads = [h for h, m in enumerate(self.masks) if m.order == TEMPORAL_MAJOR]
-        self.tm_runs = _runs(self.tm_heads)
+        # heads stored in a temporal-major order (raster or blocked patches)
+        self.tm_heads = [h for h, m in enumerate(self.masks) if m.order != FRAME_MAJOR]
+        self.tm_runs = _runs(self.tm_heads, key=lambda h: self.masks[h].order)
         self._slot = {h: i for i, h in enumerate(self.tm_heads)}
         self._buf = None
         # work counter of the persistent schedule (None: static grid)
@@ -54,7 +55,12 @@ class SparseVideoAttention:
         # fused: temporal-major heads read and write the frame-major tensors
         # through the permutation index instead of permuted copies
         self.fused = fused
-        self.perm = permutation_index(geom, device=device)[0] if fused and self.tm_heads else None
+        self.perm = None
+        if fused and self.tm_heads:
+            orders = {self.masks[h].order for h in self.tm_heads}
+            if len(orders) > 1:
+                raise SvattnError("fused: all temporal-major heads must share one token order")
+            self.perm = permutation_index(geom, device=device, order=orders.pop())[0]
 
     def _buffers(self):
         if self._buf is None:
@@ -70,7 +76,8 @@ class SparseVideoAttention:
         for a, b in self.tm_runs:
             s = self._slot[a]
             for src, dst in ((q, qt), (k, kt), (v, vt)):
-                permute_tokens(self.geom, src[a:b], out=dst[s:s + (b - a)], stream=stream)
+                permute_tokens(self.geom, src[a:b], out=dst[s:s + (b - a)], stream=stream,
+                               order=self.masks[a].order)
 
     def attend(self, q, k, v, out, scales, stream=None):
         """Forward over all heads; temporal heads read/write the scratch buffers."""
@@ -78,7 +85,7 @@ class SparseVideoAttention:
             qt, kt, vt, ot = self._buffers()
         qs, ks, vs, os_ = [], [], [], []
         for h, m in enumerate(self.masks):
-            if m.order == TEMPORAL_MAJOR:
+            if m.order != FRAME_MAJOR:
                 s = self._slot[h]
                 qs.append(qt[s]); ks.append(kt[s]); vs.append(vt[s]); os_.append(ot[s])
             else:
@@ -92,7 +99,7 @@ class SparseVideoAttention:
         ot = self._buffers()[3]
         for a, b in self.tm_runs:
             s = self._slot[a]
-            unpermute(self.geom, ot[s:s + (b - a)], out=out[a:b], stream=stream)
+            unpermute(self.geom, ot[s:s + (b - a)], out=out[a:b], stream=stream, order=self.masks[a].order)
 
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scales: Sequence[float],
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

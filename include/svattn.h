@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SVATTN_VERSION 10300 /* major*10000 + minor*100 + patch */
+#define SVATTN_VERSION 10400 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 #define SVATTN_OK 0
@@ -63,6 +63,16 @@ extern "C" {
 /* Token order a head's Q/K/V/O are stored in. */
 #define SVATTN_FRAME_MAJOR 0
 #define SVATTN_TEMPORAL_MAJOR 1   /* anchor-first; only for TEMPORAL and DENSE heads */
+/* Anchor-first temporal-major over patches listed block by block: the patch
+ * grid is cut into SVATTN_PATCH_BLOCK x SVATTN_PATCH_BLOCK blocks (the last
+ * block row and column may be smaller), blocks in raster order, patches
+ * inside a block in raster order.  Frame 0 comes first in that patch order,
+ * then each patch (same order) brings its frames 1..F-1.  A library layout,
+ * not one the pages give (they fix only that a patch's frames are adjacent):
+ * consecutive positions then cover compact patch regions, so a temporal
+ * head's tiles are fewer and less often BOUNDARY.  TEMPORAL and DENSE heads. */
+#define SVATTN_TEMPORAL_MAJOR_BLOCKED 2
+#define SVATTN_PATCH_BLOCK 4
 
 /* Tile classes stored in svattn_tile_map.cls / col_cls. */
 #define SVATTN_TILE_EMPTY 0
@@ -87,7 +97,7 @@ typedef struct {
 
 typedef struct {
   int32_t kind;   /* SVATTN_SPATIAL / SVATTN_TEMPORAL / SVATTN_DENSE */
-  int32_t order;  /* SVATTN_FRAME_MAJOR / SVATTN_TEMPORAL_MAJOR */
+  int32_t order;  /* SVATTN_FRAME_MAJOR / SVATTN_TEMPORAL_MAJOR / SVATTN_TEMPORAL_MAJOR_BLOCKED */
   int32_t window; /* spatial frame window w >= 0 (inclusive) */
   int32_t radius; /* temporal Chebyshev patch radius r >= 0 (inclusive) */
 } svattn_mask;
@@ -145,6 +155,11 @@ SVATTN_API int svattn_build_tile_map_ex(const svattn_geom* geom, const svattn_ma
  * position t'; inv[t] = position of token t (inv may be NULL).  int32 [N].
  */
 SVATTN_API int svattn_permutation_index(const svattn_geom* geom, int32_t* perm, int32_t* inv, void* stream);
+/* The same for any token order: SVATTN_TEMPORAL_MAJOR (as above),
+ * SVATTN_TEMPORAL_MAJOR_BLOCKED, or SVATTN_FRAME_MAJOR (the identity).
+ * SVATTN_ERR_INVALID_ARG for another order. */
+SVATTN_API int svattn_permutation_index_order(const svattn_geom* geom, int32_t order, int32_t* perm,
+                                              int32_t* inv, void* stream);
 
 /*
  * Reorder rows of a [heads, N, head_dim] bf16 tensor frame-major ->
@@ -156,6 +171,14 @@ SVATTN_API int svattn_permute_tokens(const svattn_geom* geom, int32_t heads, int
                           const void* src, void* dst, void* stream);
 SVATTN_API int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t head_dim,
                      const void* src, void* dst, void* stream);
+/* The same between frame-major and the temporal-major order `order`
+ * (SVATTN_TEMPORAL_MAJOR or SVATTN_TEMPORAL_MAJOR_BLOCKED; another order is
+ * SVATTN_ERR_INVALID_ARG): dst[h, t', :] = src[h, perm[t'], :] with perm from
+ * svattn_permutation_index_order, and its inverse. */
+SVATTN_API int svattn_permute_tokens_order(const svattn_geom* geom, int32_t order, int32_t heads,
+                                           int32_t head_dim, const void* src, void* dst, void* stream);
+SVATTN_API int svattn_unpermute_order(const svattn_geom* geom, int32_t order, int32_t heads, int32_t head_dim,
+                                      const void* src, void* dst, void* stream);
 
 /*
  * Block-sparse attention forward (aihirek.info, sections "A Sparse VideoGen a
@@ -210,16 +233,19 @@ SVATTN_API int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32
 /*
  * Forward with the temporal-major permutation fused in: Q, K, V, O (and lse)
  * of every head stay in frame-major order ([heads, N, head_dim] as for
- * svattn_forward), and heads whose mask has order TEMPORAL_MAJOR (maps built
- * for that order) are computed in temporal-major order by reading the rows
- * of their tensors through perm and writing their O and lse rows back through
- * it (ainews.tenesys.com, "Co się zmieniło?", item 5, without the separate
- * reordering passes).  The result equals svattn_permute_tokens, then
- * svattn_forward, then svattn_unpermute, bit for bit.
- *   perm  device int32 [N]: perm[t'] = frame-major token at temporal-major
- *         position t' (svattn_permutation_index); 4-byte aligned; may be NULL
- *         if no head runs in temporal-major order; must not overlap o, lse or
- *         the workspace.
+ * svattn_forward), and heads whose mask has a temporal-major order
+ * (TEMPORAL_MAJOR or TEMPORAL_MAJOR_BLOCKED, maps built for that order; all
+ * such heads of a call share one of the two) are computed in that order by
+ * reading the rows of their tensors through perm and writing their O and lse
+ * rows back through it (ainews.tenesys.com, "Co się zmieniło?", item 5,
+ * without the separate reordering passes).  The result equals
+ * svattn_permute_tokens_order, then svattn_forward, then
+ * svattn_unpermute_order, bit for bit.
+ *   perm  device int32 [N]: perm[t'] = frame-major token at position t' of
+ *         that order (svattn_permutation_index_order); 4-byte aligned; may be
+ *         NULL if no head runs in a temporal-major order; must not overlap o,
+ *         lse or the workspace.  SVATTN_ERR_INVALID_ARG if the call mixes the
+ *         two temporal-major orders.
  * Other arguments as for svattn_forward.
  */
 SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_dim,

@@ -26,8 +26,9 @@ def sv_mask(head: synth.Head, order=None):
     import block_sparse_spatio_svattn_amd as sv
     kind = {synth.SPATIAL: sv.SPATIAL, synth.TEMPORAL: sv.TEMPORAL, synth.DENSE: sv.DENSE}[head.kind]
     o = head.order if order is None else order
-    return sv.Mask(kind, sv.TEMPORAL_MAJOR if o == synth.TEMPORAL_MAJOR else sv.FRAME_MAJOR,
-                   head.window, head.radius)
+    orders = {synth.FRAME_MAJOR: sv.FRAME_MAJOR, synth.TEMPORAL_MAJOR: sv.TEMPORAL_MAJOR,
+              synth.TEMPORAL_MAJOR_BLOCKED: sv.TEMPORAL_MAJOR_BLOCKED}
+    return sv.Mask(kind, orders[o], head.window, head.radius)
 
 
 def errors(got: np.ndarray, ref: np.ndarray):

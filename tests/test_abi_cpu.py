@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.version() == 10300
+    assert sv.version() == 10400
     L = sv.lib()
     for code, name in [(0, b"SVATTN_OK"), (1, b"SVATTN_ERR_INVALID_ARG"), (2, b"SVATTN_ERR_UNSUPPORTED"),
                        (3, b"SVATTN_ERR_HIP"), (99, b"SVATTN_ERR_UNKNOWN")]:
@@ -84,6 +84,7 @@ def test_build_tile_map_validation():
         (sv.Mask(0, 3, 0, 0), _map(g, 64, 64), 0, INVALID),                     # bad order
         (sv.Mask(0, 0, -1, 0), _map(g, 64, 64), 0, INVALID),                    # negative window
         (sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR, 1, 0), _map(g, 64, 64), 0, UNSUPPORTED),
+        (sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR_BLOCKED, 1, 0), _map(g, 64, 64), 0, UNSUPPORTED),
         (good_mask, _map(g, 96, 64), 0, UNSUPPORTED),                           # bad block_q
         (good_mask, _map(g, 64, 64, n_qt=3), 0, INVALID),                       # wrong dims
         (good_mask, _map(g, 64, 64, col=None), 0, INVALID),                     # NULL buffer
@@ -108,6 +109,16 @@ def test_permute_validation():
     assert "overlap" in _err()
     assert L.svattn_permutation_index(ctypes.byref(g), None, None, None) == INVALID
     assert L.svattn_permutation_index(ctypes.byref(g), FAKE, FAKE + 4, None) == INVALID  # perm/inv overlap
+    # order-aware entries: frame-major cannot be permuted to, unknown orders are rejected
+    for o in (sv.FRAME_MAJOR, 3, -1):
+        assert L.svattn_permute_tokens_order(ctypes.byref(g), o, 2, 64, FAKE, FAKE * 4, None) == INVALID
+        assert "order" in _err()
+        assert L.svattn_unpermute_order(ctypes.byref(g), o, 2, 64, FAKE, FAKE * 4, None) == INVALID
+    assert L.svattn_permutation_index_order(ctypes.byref(g), 3, FAKE, None, None) == INVALID
+    assert L.svattn_permute_tokens_order(ctypes.byref(g), sv.TEMPORAL_MAJOR_BLOCKED, 2, 96, FAKE, FAKE * 4,
+                                         None) == UNSUPPORTED
+    assert L.svattn_unpermute_order(ctypes.byref(g), sv.TEMPORAL_MAJOR_BLOCKED, 2, 64, FAKE, FAKE + 64,
+                                    None) == INVALID   # overlap
 
 
 def _fwd(L, g, heads=2, d=128, masks=None, maps=None, scales=None, q=FAKE, k=FAKE * 16, v=FAKE * 32,
@@ -232,6 +243,12 @@ def test_forward_fused_validation():
     assert f(FAKE * 128 + 2) == INVALID           # misaligned
     assert f(FAKE * 64 + 1024) == INVALID         # perm inside o
     assert f(FAKE * 128, ws=FAKE * 128) == INVALID  # perm overlaps the workspace
+    # one perm cannot serve both temporal-major orders
+    mixed = (sv.Mask * heads)(sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 1),
+                              sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR_BLOCKED, 0, 1))
+    assert L.svattn_forward_fused(ctypes.byref(g), heads, d, mixed, parr, sarr, FAKE * 128, q, k, v, o, None, None,
+                                  None) == INVALID
+    assert "mixes" in _err()
     # frame-major heads only: perm may be NULL (fails later only for lack of a device)
     fm = (sv.Mask * heads)(sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.DENSE, 0, 0, 0))
     got = L.svattn_forward_fused(ctypes.byref(g), heads, d, fm, parr, sarr, None, q, k, v, o, None, None, None)

@@ -45,7 +45,7 @@ def _run_layer(sv, wl, inp, bq, bk, orders=None, flags=0):
 
 
 @pytest.mark.parametrize("bq,bk", [(32, 32), (64, 32), (32, 64), (256, 64), (128, 64)])
-@pytest.mark.parametrize("order", ["fm", "tm"])
+@pytest.mark.parametrize("order", ["fm", "tm", "tmb"])
 def test_tiny_all_rows(sv, bq, bk, order):
     wl = synth.WORKLOADS["tiny"]
     inp = synth.make_inputs(wl)
@@ -63,6 +63,19 @@ def test_small_all_rows(sv, bq, bk):
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
     for h in range(wl.n_heads):
         assert_close(f64_of(o[h]), ref[h][0], f"small h{h} {bq}x{bk}")
+
+
+@pytest.mark.parametrize("bq,bk", [(64, 64), (256, 64), (128, 32)])
+def test_small_blocked_order_all_rows(sv, bq, bk):
+    """Temporal heads in the temporal-major order over 4x4 patch blocks
+    (24 x 40 patches: whole blocks), every output row."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    orders = ["tmb" if h.kind == synth.TEMPORAL else h.order for h in wl.heads]
+    o = _run_layer(sv, wl, inp, bq, bk, orders=orders)
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"small tmb h{h} {bq}x{bk}")
 
 
 def test_small_lse_and_direct_entry(sv):
@@ -93,6 +106,20 @@ def test_full_size_sampled_rows(sv, wl_name):
     ref = _oracle_rows(wl, inp, rows)
     got = np.stack([f64_of(o[h][torch.from_numpy(rows[h]).cuda()]) for h in range(wl.n_heads)])
     assert_close(got, np.stack([r[0] for r in ref]), f"{wl_name} sampled rows")
+
+
+@pytest.mark.parametrize("wl_name", ["headline", "p1440"])
+def test_full_size_sampled_rows_blocked_order(sv, wl_name):
+    """The full-size workloads with their temporal heads in the blocked
+    temporal-major order, in the benchmark's launch configuration."""
+    wl = synth.WORKLOADS[wl_name]
+    inp = synth.make_inputs(wl)
+    rows = synth.sample_rows(wl, min(wl.sample_rows, 256))
+    orders = ["tmb" if h.kind == synth.TEMPORAL else h.order for h in wl.heads]
+    o = _run_layer(sv, wl, inp, 256, 64, orders=orders)
+    ref = _oracle_rows(wl, inp, rows)
+    got = np.stack([f64_of(o[h][torch.from_numpy(rows[h]).cuda()]) for h in range(wl.n_heads)])
+    assert_close(got, np.stack([r[0] for r in ref]), f"{wl_name} blocked order sampled rows")
 
 
 def test_perm_study_frame_major_order(sv):
@@ -298,6 +325,9 @@ def test_persistent_schedule_over_several_launches(sv):
     ((17, 3, 16), 1, "fm", 128, 64),  # W = 16: patch-row runs, frame-major
     ((5, 6, 40), 3, "fm", 64, 32),
     ((3, 2, 70), 9, "fm", 256, 64),   # rows longer than a tile
+    ((21, 4, 6), 1, "tmb", 256, 64),  # blocked patch order: 4x4 and 4x2 blocks
+    ((17, 9, 13), 2, "tmb", 128, 64), # ragged blocks in both directions, F-1 = 16
+    ((21, 5, 7), 1, "tmb", 64, 32),
 ])
 def test_long_run_masks_all_rows(sv, geom, r, order, bq, bk):
     """Geometries whose key runs (F-1 frames of a patch in temporal-major order,
@@ -335,7 +365,7 @@ def test_tile_aligned_long_runs(sv):
     """Tile snapping with key runs of 20 frames (the headline's F - 1) and a
     ragged tail, temporal-major and frame-major temporal heads."""
     heads = (synth.Head("temporal", radius=1, order="tm"), synth.Head("temporal", radius=2, order="fm"),
-             synth.Head("spatial", window=1))
+             synth.Head("spatial", window=1), synth.Head("temporal", radius=1, order="tmb"))
     wl = synth.Workload(name="ta", seed=29, frames=21, height=4, width=6, head_dim=128, heads=heads,
                         tiles=((128, 64),))
     inp = synth.make_inputs(wl)
@@ -364,6 +394,30 @@ def test_fused_permutation_bit_identical(sv, wl_name, bq, bk, persistent):
     o_fused = SparseVideoAttention(g, masks, wl.head_dim, bq, bk, persistent=persistent, fused=True)(q, k, v, scales)
     torch.cuda.synchronize()
     assert (bits_of(o_sep) == bits_of(o_fused)).all()
+
+
+@pytest.mark.parametrize("geom,bq,bk", [((4, 8, 8), 256, 64), ((5, 24, 40), 128, 64), ((17, 9, 13), 64, 32)])
+def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk):
+    """Fused and separate paths agree bit for bit with the temporal heads in the
+    blocked order; both within the bar of the oracle."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    heads = (synth.Head("spatial", window=1), synth.Head("temporal", radius=2, order="tmb"),
+             synth.Head("temporal", radius=1, order="tmb"))
+    F, H, W = geom
+    wl = synth.Workload(name="fb", seed=37, frames=F, height=H, width=W, head_dim=128, heads=heads,
+                        tiles=((bq, bk),))
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(F, H, W)
+    masks = [sv_mask(h) for h in heads]
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    o_sep = SparseVideoAttention(g, masks, 128, bq, bk)(q, k, v, scales)
+    o_fused = SparseVideoAttention(g, masks, 128, bq, bk, fused=True)(q, k, v, scales)
+    torch.cuda.synchronize()
+    assert (bits_of(o_sep) == bits_of(o_fused)).all()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * len(heads))
+    for h in range(len(heads)):
+        assert_close(f64_of(o_fused[h]), ref[h][0], f"fused tmb {geom} h{h}")
 
 
 def test_fused_permutation_lse_and_ragged_long_runs(sv):

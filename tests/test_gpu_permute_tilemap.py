@@ -19,28 +19,31 @@ def sv():
     return m
 
 
-@pytest.mark.parametrize("F,H,W", GEOMS)
-def test_permutation_index_bit_exact(sv, F, H, W):
+@pytest.mark.parametrize("order", ["tm", "tmb"])
+@pytest.mark.parametrize("F,H,W", GEOMS + [(3, 9, 13), (4, 13, 17)])
+def test_permutation_index_bit_exact(sv, F, H, W, order):
     g = sv.Geom(F, H, W)
-    perm, inv = sv.permutation_index(g)
-    ref = oracle.temporal_major_perm(oracle.Geometry(F, H, W))
+    perm, inv = sv.permutation_index(g, order=sv.TEMPORAL_MAJOR if order == "tm" else sv.TEMPORAL_MAJOR_BLOCKED)
+    ref = oracle.layout_tokens(oracle.Geometry(F, H, W), order)
     p = perm.cpu().numpy()
     assert (p == ref).all()
     iv = inv.cpu().numpy()
     assert (iv[ref] == np.arange(g.n)).all()
 
 
+@pytest.mark.parametrize("order", ["tm", "tmb"])
 @pytest.mark.parametrize("F,H,W,d,heads", [(4, 8, 8, 64, 2), (5, 24, 40, 128, 3), (3, 5, 7, 128, 2),
-                                           (21, 45, 80, 128, 5), (1, 4, 4, 64, 1)])
-def test_permute_unpermute_bit_exact(sv, F, H, W, d, heads):
+                                           (21, 45, 80, 128, 5), (1, 4, 4, 64, 1), (3, 9, 13, 64, 2)])
+def test_permute_unpermute_bit_exact(sv, F, H, W, d, heads, order):
     g = sv.Geom(F, H, W)
     x = synth.random_bf16((heads, g.n, d), seed=F * 1000 + W)
     xd = to_dev(x)
-    perm = oracle.temporal_major_perm(oracle.Geometry(F, H, W))
-    y = sv.permute_tokens(g, xd)
+    perm = oracle.layout_tokens(oracle.Geometry(F, H, W), order)
+    o = sv.TEMPORAL_MAJOR if order == "tm" else sv.TEMPORAL_MAJOR_BLOCKED
+    y = sv.permute_tokens(g, xd, order=o)
     torch.cuda.synchronize()
     assert (bits_of(y) == x[:, perm]).all()
-    back = sv.unpermute(g, y)
+    back = sv.unpermute(g, y, order=o)
     torch.cuda.synchronize()
     assert (bits_of(back) == x).all()
 
@@ -90,6 +93,12 @@ SMALL_CASES = (
     + [((3, 5, 7), "temporal", 0, 1, "tm", 32, 32), ((3, 5, 7), "spatial", 1, 0, "fm", 64, 32),
        ((1, 4, 4), "temporal", 0, 1, "tm", 32, 32), ((7, 1, 9), "temporal", 0, 2, "tm", 32, 64),
        ((2, 3, 5), "spatial", 0, 0, "fm", 32, 128)]
+    # temporal-major over 4x4 patch blocks, with ragged edge blocks and tiles
+    + [(geom, "temporal", 0, r, "tmb", bq, bk)
+       for geom, r in [((4, 8, 8), 1), ((5, 24, 40), 2), ((3, 9, 13), 2), ((3, 5, 7), 1), ((7, 1, 9), 2),
+                       ((1, 4, 4), 1), ((4, 13, 17), 5)]
+       for bq, bk in [(32, 32), (128, 64), (256, 64)]]
+    + [((4, 8, 8), "dense", 0, 0, "tmb", 64, 64)]
 )
 
 
@@ -105,7 +114,8 @@ def test_tile_map_bit_exact(sv, geom, kind, w, r, order, bq, bk):
 
 @pytest.mark.parametrize("wl_name,hi,order", [("headline", 0, "fm"), ("headline", 5, "tm"),
                                               ("headline", 5, "fm"), ("perm_study", 0, "tm"),
-                                              ("p1440", 0, "fm"), ("p1440", 5, "tm")])
+                                              ("p1440", 0, "fm"), ("p1440", 5, "tm"), ("headline", 5, "tmb"),
+                                              ("perm_study", 0, "tmb"), ("p1440", 5, "tmb")])
 @pytest.mark.parametrize("bq,bk", [(256, 64), (128, 32)])
 def test_tile_map_large_sampled_rows(sv, wl_name, hi, order, bq, bk):
     wl = synth.WORKLOADS[wl_name]
