@@ -458,34 +458,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             // run: the F-1 frames of one patch (p: the patch's rank in the
             // order's patch sequence)
             const int F1 = g.F - 1;
-            int p = (int)g.divF1.div((uint32_t)(s0 + key0 - g.P));
+            const int p = (int)g.divF1.div((uint32_t)(s0 + key0 - g.P));
             int rs = s0, re = g.P + (p + 1) * F1 - key0;
+            // The first run's patch is decomposed once (raster order: row and
+            // column; blocked order: block row, block column, row and column
+            // in the block); later runs step to the next patch of the order
+            // (runs past the last patch hold no key).  Every wave of the
+            // workgroup runs this on the compute unit's one scalar unit, so
+            // it avoids a division per run.
+            const bool blk = order == SVATTN_TEMPORAL_MAJOR_BLOCKED;
+            int by, bx;
+            if (blk) {
+              blocked_yx(g, p, by, bx);
+            } else {
+              by = (int)g.divW.div((uint32_t)p);
+              bx = p - by * g.W;
+            }
+            int tr = by >> 2, tc = bx >> 2, iy = by & 3, ix = bx & 3;
+            int bh = tr == g.NBR - 1 ? g.HL : kPatchBlock, bw = tc == g.NBC - 1 ? g.WL : kPatchBlock;
 #pragma unroll
             for (int i = 0; i < MAXR; ++i) {
-              int y, x;
-              if (order == SVATTN_TEMPORAL_MAJOR_BLOCKED) {
-                blocked_yx(g, min(p, g.P - 1), y, x);  // runs past the last patch hold no key
-              } else {
-                y = (int)g.divW.div((uint32_t)p);
-                x = p - y * g.W;
-              }
+              const int y = blk ? tr * kPatchBlock + iy : by;
+              const int x = blk ? tc * kPatchBlock + ix : bx;
               const uint64_t rb = bit_range(rs, min(re, e0));
 #pragma unroll
               for (int gq = 0; gq < QG; ++gq) {
                 const bool k = ((uint32_t)(y - mq_a[gq] + r) <= r2) & ((uint32_t)(x - mq_b[gq] + r) <= r2);
                 keep[gq] |= k ? rb : 0ull;
               }
-              ++p;
+              if (blk) {
+                if (++ix == bw) {
+                  ix = 0;
+                  if (++iy == bh) {
+                    iy = 0;
+                    if (++tc == g.NBC) {
+                      tc = 0;
+                      ++tr;
+                      bh = tr == g.NBR - 1 ? g.HL : kPatchBlock;
+                    }
+                    bw = tc == g.NBC - 1 ? g.WL : kPatchBlock;
+                  }
+                }
+              } else if (++bx == g.W) {
+                bx = 0;
+                ++by;
+              }
               rs = re;
               re += F1;
             }
           } else {
-            // run: one patch row of one frame; x advances with the key
+            // run: one patch row of one frame; x advances with the key.  The
+            // first run's row and column are divided out once; every later
+            // run starts a new row at column 0 (the row after the last one
+            // of a frame is row 0 of the next frame).
             int rs = s0;
+            const int pp = (int)g.divP.mod((uint32_t)(key0 + rs));
+            int y = (int)g.divW.div((uint32_t)pp), x0 = pp - y * g.W;
 #pragma unroll
             for (int i = 0; i < MAXR; ++i) {
-              const int pp = (int)g.divP.mod((uint32_t)(key0 + rs));
-              const int y = (int)g.divW.div((uint32_t)pp), x0 = pp - y * g.W;
               const int re = min(rs + (g.W - x0), e0);
 #pragma unroll
               for (int gq = 0; gq < QG; ++gq) {
@@ -494,6 +524,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 keep[gq] |= ky ? bit_range(max(lo, rs), min(hi, re)) : 0ull;
               }
               rs = max(re, rs);
+              x0 = 0;
+              y = y + 1 == g.H ? 0 : y + 1;
             }
           }
         }
