@@ -476,11 +476,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
             int tr = by >> 2, tc = bx >> 2, iy = by & 3, ix = bx & 3;
             int bh = tr == g.NBR - 1 ? g.HL : kPatchBlock, bw = tc == g.NBC - 1 ? g.WL : kPatchBlock;
+            // run i covers keys [b_i, b_i+1) clipped to e0: its bits are
+            // below(b_i+1) & ~below(b_i), each prefix mask shared by two runs
+            auto below = [](int b) __attribute__((always_inline)) -> uint64_t {
+              return b >= 64 ? ~0ull : ((1ull << b) - 1ull);
+            };
+            uint64_t lo = below(rs);
 #pragma unroll
             for (int i = 0; i < MAXR; ++i) {
               const int y = blk ? tr * kPatchBlock + iy : by;
               const int x = blk ? tc * kPatchBlock + ix : bx;
-              const uint64_t rb = bit_range(rs, min(re, e0));
+              const uint64_t hi = below(min(re, e0));
+              const uint64_t rb = hi & ~lo;
+              lo = hi;
 #pragma unroll
               for (int gq = 0; gq < QG; ++gq) {
                 const bool k = ((uint32_t)(y - mq_a[gq] + r) <= r2) & ((uint32_t)(x - mq_b[gq] + r) <= r2);
