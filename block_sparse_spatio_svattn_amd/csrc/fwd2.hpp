@@ -293,29 +293,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  // HBM -> LDS copies of K and V tiles.  A stage is OPS 1 KB pieces; lane L
-  // of a piece fills byte 16 L of it, i.e. one 16-byte chunk slot of a row,
-  // and fetches that chunk of the key's row (K padding slots fetch the tile's
-  // first chunk).  Copier wave c owns pieces c, c + NCW, ....  A copy
+  // HBM -> LDS copies of K and V tiles.  A stage is K_PIECES + V_PIECES 1 KB
+  // pieces; lane L of a piece fills byte 16 L of it, i.e. one 16-byte chunk
+  // slot of a row, and fetches that chunk of the key's row (K padding slots
+  // fetch the tile's first chunk).  Copier wave c copies K pieces c, c + NCW,
+  // ... with its first KOPS copies and V pieces c, c + NCW, ... with the
+  // rest, so whether a copy reads K or V is fixed at compile time.  A copy
   // blocks its wave until the vector-memory queue takes it, so the copies go
   // where a wave has no LDS reads in flight and, in the two-group schedule,
   // trickle through the softmax of the group without MFMA work.  They are
   // inline asm, so the compiler adds no wait for them before the LDS reads of
   // other stages; explicit waits precede the barriers.
-  constexpr int OPS = C::K_PIECES + C::V_PIECES;
   constexpr int NCW = PP ? NW / 2 : NW;       // copier waves: group B, or all
-  constexpr int OPC = (OPS + NCW - 1) / NCW;  // pieces per copier wave
+  constexpr int KOPS = (C::K_PIECES + NCW - 1) / NCW;
+  constexpr int VOPS = (C::V_PIECES + NCW - 1) / NCW;
+  constexpr int OPC = KOPS + VOPS;            // copies per copier wave
   const int cw = PP ? wave_u - NW / 2 : wave_u;  // index among the copiers
-  // Byte offset, from the tile's first row, of the chunk each of this lane's
-  // pieces fetches.  A copy then needs no vector arithmetic: the tile's first
-  // row is a scalar base and the lane offset is precomputed (the rows past N
-  // of a ragged tile are clamped at issue instead).
+  // Piece (within K or V) and byte offset, from the tile's first row, of the
+  // chunk each of this lane's copies fetches.  A copy then needs no vector
+  // arithmetic: the tile's first row is a scalar base and the lane offset is
+  // precomputed (the rows past N of a ragged tile are clamped at issue).
+  auto op_piece = [&](int i) __attribute__((always_inline)) { return cw + (i < KOPS ? i : i - KOPS) * NCW; };
   int dma_off[OPC];
 #pragma unroll
   for (int i = 0; i < OPC; ++i) {
-    const int o = cw + i * NCW;
-    const bool is_k = o < C::K_PIECES;
-    const int byte = (is_k ? o : o - C::K_PIECES) * 1024 + lane * 16;
+    const bool is_k = i < KOPS;
+    const int byte = op_piece(i) * 1024 + lane * 16;
     const int rb = is_k ? C::RBK : C::RBV;
     const int row = byte / rb, slot = (byte - row * rb) >> 4;
     const bool real = row < BK && slot < C::CPR;
@@ -332,11 +335,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int i = 0; i < OPC; ++i) prow[i] = hd.perm[min(key0 + dma_off[i] / (D * 2), N - 1)];
     }
   };
-  // Piece i of this wave for the tile starting at key0, into stage st.
-  auto issue_op = [&](int i, int key0, int st) __attribute__((always_inline)) {
-    const int o = cw + i * NCW;
-    if (cw < 0 || (OPS % NCW != 0 && o >= OPS)) return;
-    const bool is_k = o < C::K_PIECES;
+  // Copy i of this wave for the tile starting at key0, into stage st (ragged:
+  // the tile runs past the last token).
+  auto issue_op = [&](int i, int key0, int st, bool ragged) __attribute__((always_inline)) {
+    const bool is_k = i < KOPS;
+    const int pc = op_piece(i);
+    if (cw < 0) return;
+    if ((is_k && C::K_PIECES % NCW != 0 && i == KOPS - 1 && pc >= C::K_PIECES) ||
+        (!is_k && C::V_PIECES % NCW != 0 && i == OPC - 1 && pc >= C::V_PIECES))
+      return;
     // The tile's first row (or, gathered, the head's first row) as a scalar
     // base address (uniform by construction; readfirstlane makes that
     // explicit for the asm's SGPR operand).
@@ -346,11 +353,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     uint32_t off = (uint32_t)dma_off[i];
     if (gathered) {  // row prow[i] of the tensor, same chunk
       if constexpr (GTH) off = (uint32_t)(prow[i] * (D * 2) + (dma_off[i] % (D * 2)));
-    } else if (key0 + BK > N) {  // ragged tile: rows past N read row N-1 (their keys are masked)
+    } else if (ragged) {  // rows past N read row N-1 (their keys are masked)
       const int row = (int)(off / (D * 2));
       off = (uint32_t)((min(key0 + row, N - 1) - key0) * (D * 2) + (off - row * (D * 2)));
     }
-    const uint32_t dst = lds_base + st * C::STAGE_BYTES + o * 1024;
+    const uint32_t dst = lds_base + st * C::STAGE_BYTES + ((is_k ? 0 : C::K_PIECES) + pc) * 1024;
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(base) : "m0");
   };
   // Key coordinates of temporal heads for the tile starting at key0 (the
@@ -359,10 +366,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int t = tid - (PP ? NW / 2 : 0) * 64;
     if (need_kc && t >= 0 && t < BK) kcs[st][t] = fwd2::key_coord(g, order, key0 + t);
   };
-  // All copies of a tile at once (prologue).
+  // All copies of a tile at once (one branch for a ragged tile).
   auto issue = [&](int key0, int st) __attribute__((always_inline)) {
+    if (key0 + BK > N) {
 #pragma unroll
-    for (int i = 0; i < OPC; ++i) issue_op(i, key0, st);
+      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, true);
+    } else {
+#pragma unroll
+      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, false);
+    }
     issue_kc(key0, st);
   };
   // All of this wave's copies have landed in LDS (the barrier that follows
@@ -691,7 +703,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (!dma) return;
 #pragma unroll
     for (int i = 0; i < OPC; ++i)
-      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st);
+      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st, key0 + BK > N);
   };
   auto next_stage = [&](int st) __attribute__((always_inline)) { return st == STAGES - 1 ? 0 : st + 1; };
 
