@@ -78,12 +78,14 @@ struct Cfg {
 };
 
 // Fragments of K (KPF) and of V (VPF) read from LDS ahead of the MFMA that
-// consumes them.
+// consumes them.  Without the explicit prefetch (and the fences that hold
+// it), the scheduler placed each read right before its MFMA and waited for
+// it there, so every MFMA of the plain schedule waited out one LDS latency.
 #ifndef SVATTN_KPF
-#define SVATTN_KPF 4
+#define SVATTN_KPF 6
 #endif
 #ifndef SVATTN_VPF
-#define SVATTN_VPF 3
+#define SVATTN_VPF 4
 #endif
 constexpr int KPF = SVATTN_KPF;
 constexpr int VPF = SVATTN_VPF;
@@ -381,34 +383,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // makes every wave's copies visible).
   auto wait_tiles = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  // S^T = K Q^T for the tile in stage st.
+  // S^T = K Q^T for the tile in stage st.  K fragments are read KPF MFMAs
+  // ahead of their use; a scheduling fence after each MFMA keeps that order.
   auto qk = [&](int st, floatx16 (&S)[C::KB][QG], auto&& after_mfma) __attribute__((always_inline)) {
     const char* Ks = smem + st * C::STAGE_BYTES;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int gq = 0; gq < QG; ++gq) S[kb][gq] = floatx16{};
-#pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + kb * 32 * C::RBK + koff + ds * 32);
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq)
-          S[kb][gq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[gq][ds], S[kb][gq], 0, 0, 0);
-        after_mfma(ds * C::KB + kb);
-      }
-    }
-    // Interleave: KPF fragments ahead, then one MFMA group per fragment, so
-    // only a few K fragments are in registers at a time.
     constexpr int NR = C::DS * C::KB;
-    __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+    auto ld = [&](int r) __attribute__((always_inline)) {
+      const int ds = r / C::KB, kb = r % C::KB;
+      return *(const bf16x8*)(Ks + kb * 32 * C::RBK + koff + ds * 32);
+    };
+    constexpr int PF = KPF < NR ? KPF : NR;  // prefetch depth, at most the fragment count
+    bf16x8 kf[NR];
 #pragma unroll
-    for (int i = 0; i < NR - KPF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int r = 0; r < PF; ++r) kf[r] = ld(r);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int ds = r / C::KB, kb = r % C::KB;
+      if (r + PF < NR) kf[r + PF] = ld(r + PF);
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+        S[kb][gq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[r], qf[gq][ds], ds == 0 ? floatx16{} : S[kb][gq], 0, 0, 0);
+      after_mfma(r);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, KPF * QG, 0);
   };
 
   // Coordinate mask of the tile in stage st (boundary and ragged tiles only).
@@ -663,35 +660,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  // O^T += V^T P^T for the tile in stage st.
+  // O^T += V^T P^T for the tile in stage st.  V^T fragments (two transpose
+  // reads each) are read VPF MFMAs ahead of their use, fenced like qk.
   auto pv = [&](int st, const bf16x8 (&P)[2 * C::KB][QG], auto&& after_mfma) __attribute__((always_inline)) {
     const char* Vs = smem + st * C::STAGE_BYTES + C::K_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < 2 * C::KB; ++ks) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const char* base = Vs + ks * 16 * C::RBV + voff[db];
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(base));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(base + 8 * C::RBV));
-        const short4v both[2] = {lo, hi};
-        bf16x8 va;
-        __builtin_memcpy(&va, both, sizeof(va));
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq)
-          acc[gq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[ks][gq], acc[gq][db], 0, 0, 0);
-        after_mfma(ks * C::DB + db);
-      }
-    }
-    // Interleave the transpose reads (two per fragment) with the MFMAs,
-    // VPF fragments ahead.
     constexpr int NR = 2 * C::KB * C::DB;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+    auto ld = [&](int r) __attribute__((always_inline)) {
+      const int ks = r / C::DB, db = r % C::DB;
+      const char* base = Vs + ks * 16 * C::RBV + voff[db];
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(base));
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(base + 8 * C::RBV));
+      const short4v both[2] = {lo, hi};
+      bf16x8 va;
+      __builtin_memcpy(&va, both, sizeof(va));
+      return va;
+    };
+    constexpr int PF = VPF < NR ? VPF : NR;
+    bf16x8 vf[NR];
 #pragma unroll
-    for (int i = 0; i < NR - VPF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int r = 0; r < PF; ++r) vf[r] = ld(r);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int ks = r / C::DB, db = r % C::DB;
+      if (r + PF < NR) vf[r + PF] = ld(r + PF);
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+        acc[gq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[r], P[ks][gq], acc[gq][db], 0, 0, 0);
+      after_mfma(r);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, VPF * QG, 0);
   };
 
   floatx16 S[C::KB][QG];
