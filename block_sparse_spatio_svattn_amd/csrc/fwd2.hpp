@@ -464,65 +464,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int e0 = min(BK, lim_n);         // past the last key of the tile
         if (s0 < e0) {
           if (order != SVATTN_FRAME_MAJOR) {
-            // run: the F-1 frames of one patch (p: the patch's rank in the
-            // order's patch sequence)
+            // run: the F-1 frames of one patch.  Lane i works out run i of
+            // the tile (its patch's rank in the order's patch sequence, the
+            // patch's row and column, and its key range as a 64-bit mask);
+            // the wave then reads each run's values back as scalars and
+            // every lane tests its own query against them.  The run
+            // arithmetic is the same for every wave, and in vector lanes it
+            // does not queue on the compute unit's one scalar unit.
             const int F1 = g.F - 1;
-            const int p = (int)g.divF1.div((uint32_t)(s0 + key0 - g.P));
-            int rs = s0, re = g.P + (p + 1) * F1 - key0;
-            // The first run's patch is decomposed once (raster order: row and
-            // column; blocked order: block row, block column, row and column
-            // in the block); later runs step to the next patch of the order
-            // (runs past the last patch hold no key).  Every wave of the
-            // workgroup runs this on the compute unit's one scalar unit, so
-            // it avoids a division per run.
-            const bool blk = order == SVATTN_TEMPORAL_MAJOR_BLOCKED;
-            int by, bx;
-            if (blk) {
-              blocked_yx(g, p, by, bx);
+            const int p0 = (int)g.divF1.div((uint32_t)(s0 + key0 - g.P));  // the first run's patch rank
+            const int pr = p0 + (lane < MAXR ? lane : 0);
+            const int rs = max(g.P + pr * F1 - key0, s0);
+            const int re = min(g.P + (pr + 1) * F1 - key0, e0);  // empty when re <= rs (past the last patch)
+            int ry, rx;
+            if (order == SVATTN_TEMPORAL_MAJOR_BLOCKED) {
+              blocked_yx(g, pr, ry, rx);
             } else {
-              by = (int)g.divW.div((uint32_t)p);
-              bx = p - by * g.W;
+              ry = (int)g.divW.div((uint32_t)pr);
+              rx = pr - ry * g.W;
             }
-            int tr = by >> 2, tc = bx >> 2, iy = by & 3, ix = bx & 3;
-            int bh = tr == g.NBR - 1 ? g.HL : kPatchBlock, bw = tc == g.NBC - 1 ? g.WL : kPatchBlock;
-            // run i covers keys [b_i, b_i+1) clipped to e0: its bits are
-            // below(b_i+1) & ~below(b_i), each prefix mask shared by two runs
-            auto below = [](int b) __attribute__((always_inline)) -> uint64_t {
-              return b >= 64 ? ~0ull : ((1ull << b) - 1ull);
+            // bits [rs, re) of the tile's 64 keys, as two 32-bit halves
+            auto below32 = [](int b) __attribute__((always_inline)) -> uint32_t {
+              return b <= 0 ? 0u : b >= 32 ? 0xffffffffu : (1u << b) - 1u;
             };
-            uint64_t lo = below(rs);
+            const uint32_t rlo = below32(re) & ~below32(rs);
+            const uint32_t rhi = below32(re - 32) & ~below32(rs - 32);
+            uint32_t klo[QG], khi[QG];
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq) {
+              klo[gq] = 0u;
+              khi[gq] = 0u;
+            }
 #pragma unroll
             for (int i = 0; i < MAXR; ++i) {
-              const int y = blk ? tr * kPatchBlock + iy : by;
-              const int x = blk ? tc * kPatchBlock + ix : bx;
-              const uint64_t hi = below(min(re, e0));
-              const uint64_t rb = hi & ~lo;
-              lo = hi;
+              const int y = __builtin_amdgcn_readlane(ry, i);
+              const int x = __builtin_amdgcn_readlane(rx, i);
+              const uint32_t blo = (uint32_t)__builtin_amdgcn_readlane((int)rlo, i);
+              const uint32_t bhi = (uint32_t)__builtin_amdgcn_readlane((int)rhi, i);
 #pragma unroll
               for (int gq = 0; gq < QG; ++gq) {
                 const bool k = ((uint32_t)(y - mq_a[gq] + r) <= r2) & ((uint32_t)(x - mq_b[gq] + r) <= r2);
-                keep[gq] |= k ? rb : 0ull;
+                klo[gq] |= k ? blo : 0u;
+                khi[gq] |= k ? bhi : 0u;
               }
-              if (blk) {
-                if (++ix == bw) {
-                  ix = 0;
-                  if (++iy == bh) {
-                    iy = 0;
-                    if (++tc == g.NBC) {
-                      tc = 0;
-                      ++tr;
-                      bh = tr == g.NBR - 1 ? g.HL : kPatchBlock;
-                    }
-                    bw = tc == g.NBC - 1 ? g.WL : kPatchBlock;
-                  }
-                }
-              } else if (++bx == g.W) {
-                bx = 0;
-                ++by;
-              }
-              rs = re;
-              re += F1;
             }
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq) keep[gq] |= ((uint64_t)khi[gq] << 32) | klo[gq];
           } else {
             // run: one patch row of one frame; x advances with the key.  The
             // first run's row and column are divided out once; every later
