@@ -43,9 +43,10 @@
 //
 // Softmax.  exp2 with the scale folded into one FMA; masked scores are -inf.
 // The running max only moves when a new score exceeds it by more than 8 in
-// log2 units, so most tiles skip rescaling the accumulator; the result differs
-// only by rounding.  P is rounded to bf16 for the P V product; the row sum
-// (and so lse) accumulates the fp32 values.
+// log2 units, so most tiles skip rescaling the accumulator, and a tile whose
+// exponentials all stay within 2^8 of the running max needs no max reduction
+// at all; the result differs only by rounding.  P is rounded to bf16 for the
+// P V product; the row sum (and so lse) accumulates the fp32 values.
 #pragma once
 
 #include <type_traits>
@@ -92,6 +93,7 @@ constexpr int VPF = SVATTN_VPF;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kSumBound = 256.0f;         // 2^kRescaleThreshold
 constexpr float kNegBig = -1.0e30f;        // initial running max (finite)
 
 // XOR applied to the chunk index of V row r (an involution for a fixed row).
@@ -608,40 +610,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
   // Online softmax of one tile's scores; P (bf16) is the B operand of P V.
+  // The exponentials are first taken against the running max as it stands.
+  // If every lane's partial row sum stays within 2^8 (so no exponential
+  // exceeds 2^8), the tile's max cannot have passed the running max by more
+  // than the rescale threshold, and the values stand as computed: the usual
+  // case, with no max reduction.  Otherwise (the first tile of a row, whose
+  // running max is still the initial value, or a tile with larger scores)
+  // the exact tile max is taken, the accumulator is rescaled if the max moves,
+  // and the exponentials are taken again.
   auto softmax = [&](floatx16 (&S)[C::KB][QG], bf16x8 (&P)[2 * C::KB][QG], auto&& after_chunk) __attribute__((always_inline)) {
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
-      float mx = -INFINITY;
+      auto exps = [&](auto&& hook) __attribute__((always_inline)) -> float {
+        const float mc = m_run[gq] * c;
+        float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+        for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][gq][i]);
-      mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run[gq], mx);
-      const bool need = (m_new - m_run[gq]) * c > kRescaleThreshold;
-      if (__any(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f((m_run[gq] - m_new) * c) : 1.0f;
-        if (need) m_run[gq] = m_new;
-        l_run[gq] *= alpha;
+          for (int h = 0; h < 2; ++h) {
+            bf16x8 p;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[gq][db] *= alpha;
-      }
-      const float mc = m_run[gq] * c;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 p;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][gq][h * 8 + j], c, -mc));
-            ls += e;
-            p[j] = (__bf16)e;
+            for (int j = 0; j < 8; ++j) {
+              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][gq][h * 8 + j], c, -mc));
+              ls += e;
+              p[j] = (__bf16)e;
+            }
+            P[kb * 2 + h][gq] = p;
+            hook((gq * C::KB + kb) * 2 + h);
           }
-          P[kb * 2 + h][gq] = p;
-          after_chunk((gq * C::KB + kb) * 2 + h);
         }
+        return ls;
+      };
+      float ls = exps(after_chunk);
+      if (__any(!(ls <= kSumBound))) {  // also true for inf and NaN
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][gq][i]);
+        mx = max_xor32(mx);
+        const float m_new = fmaxf(m_run[gq], mx);
+        const bool need = (m_new - m_run[gq]) * c > kRescaleThreshold;
+        if (__any(need)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f((m_run[gq] - m_new) * c) : 1.0f;
+          if (need) m_run[gq] = m_new;
+          l_run[gq] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) acc[gq][db] *= alpha;
+        }
+        ls = exps([](int) {});
       }
       l_run[gq] += ls;
     }
