@@ -35,8 +35,9 @@
 // swizzle gives each of those rows its own banks.
 //
 // Schedules.  The plain schedule (PP = false) runs every wave through
-// S, mask, softmax and P V of a tile, then one barrier; K/V of the next tile
-// stream into the other half of a double buffer meanwhile.  The two-group
+// S, mask, softmax and P V of a tile (of two tiles, for the d128 256 x 64
+// launch), then one barrier; K/V of the next tile(s) stream into the other
+// half of an LDS ring meanwhile.  The two-group
 // schedule (PP = true, 8 waves) offsets waves 4-7 by half a tile so that on
 // each SIMD one wave's MFMA work overlaps the other wave's softmax; it keeps a
 // ring of three K/V stages (see the loop).
@@ -150,7 +151,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   static_assert(BK % 32 == 0 && (D == 64 || D == 128), "tile shape");
   static_assert(!PP || NW == 8, "the two-group schedule pairs waves w and w + 4 on one SIMD");
   static_assert(!GTH || (!PP && !BITS), "gathered heads run the plain schedule over tile maps");
-  constexpr int STAGES = PP ? 3 : 2;
+  // Tiles per barrier of the plain schedule: the d128, 256 x 64 launch runs
+  // two tiles between barriers (four LDS stages, 132 KB), the others one.
+  constexpr int TPB = (!PP && !GTH && !BITS && D == 128 && BK == 64 && NW == 8) ? 2 : 1;
+  constexpr int STAGES = PP ? 3 : 2 * TPB;
   __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
 
@@ -773,44 +777,68 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (grp_b) run(std::true_type{});
     else run(std::false_type{});
   } else {
-    // Every wave: S, mask and softmax of tile j, then the copies of tile j+1
-    // (into the stage of tile j-1; the wave has no LDS reads in flight here),
-    // then P V of tile j and one barrier.
+    // Tiles go in groups of TPB between two barriers, over a ring of 2 TPB
+    // stages: group g reads stages (g % 2) TPB + u, u < TPB.  Every wave
+    // runs S, mask and softmax of a tile, then the copies of the tile TPB
+    // places later (into the other half of the ring, whose readers finished
+    // before the last barrier; the wave has no LDS reads in flight here),
+    // then P V; one barrier ends the group.
+    // Tile list window: wk/wc[0] is the current tile, [TPB] the one whose
+    // copies go out with it, [TPB + 1] fetched ahead.
+    int wk[TPB + 2], wc[TPB + 2];
+#pragma unroll
+    for (int i = 0; i < TPB + 2; ++i) {
+      wk[i] = 0;
+      wc[i] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i <= TPB; ++i) fetch(i, wk[i], wc[i]);
     if (n > 0) {
       if constexpr (GTH)
-        if (gathered) gather_rows(key_c);
-      issue(key_c, 0);
+        if (gathered) gather_rows(wk[0]);
+      issue(wk[0], 0);
     }
+    if constexpr (TPB == 2)
+      if (n > 1) issue(wk[1], 1);
     wait_tiles();
     __syncthreads();
-    int st = 0;  // stage of tile j
-    for (int j = 0; j < n; ++j) {
-      int key_nn = 0, cls_nn = 0;
-      fetch(j + 2, key_nn, cls_nn);
-      if constexpr (GTH)
-        if (gathered && j + 1 < n) gather_rows(key_n);
-      // a wave whose queries keep no key of this tile skips S, softmax and P V
-      uint64_t keep[QG];
-      const int ms = plan(key_c, cls_c, keep);
-      if (ms != 2) {
-        qk(st, S, [](int) {});
-        if (ms == 0) {
+    int grp = 0;  // first stage of the current group
+    for (int j = 0; j < n; j += TPB) {
 #pragma unroll
-          for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
-        } else if (ms == 3) {
-          mask_scores(st, key_c, S);
+      for (int u = 0; u < TPB; ++u) {
+        const int t = j + u;
+        if (u == 0 || t < n) {
+          const int st = grp + u;
+          fetch(t + TPB + 1, wk[TPB + 1], wc[TPB + 1]);
+          if constexpr (GTH)
+            if (gathered && t + 1 < n) gather_rows(wk[1]);
+          // a wave whose queries keep no key of this tile skips S, softmax and P V
+          uint64_t keep[QG];
+          const int ms = plan(wk[0], wc[0], keep);
+          if (ms != 2) {
+            qk(st, S, [](int) {});
+            if (ms == 0) {
+#pragma unroll
+              for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
+            } else if (ms == 3) {
+              mask_scores(st, wk[0], S);
+            }
+            softmax(S, P, [](int) {});
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + TPB < n) issue(wk[TPB], (grp ^ TPB) + u);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ms != 2) pv(st, P, [](int) {});
+#pragma unroll
+          for (int i = 0; i <= TPB; ++i) {
+            wk[i] = wk[i + 1];
+            wc[i] = wc[i + 1];
+          }
         }
-        softmax(S, P, [](int) {});
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 < n) issue(key_n, next_stage(st));
-      __builtin_amdgcn_sched_barrier(0);
-      if (ms != 2) pv(st, P, [](int) {});
       wait_tiles();
       __syncthreads();
-      key_c = key_n; cls_c = cls_n;
-      key_n = key_nn; cls_n = cls_nn;
-      st = next_stage(st);
+      grp ^= TPB;
     }
   }
 
