@@ -101,10 +101,12 @@ int check_map_buffers(const svattn_tile_map* map, const char* who) {
   return SVATTN_OK;
 }
 
-// Schedule choice: the two-group schedule (one wave's MFMA work beside its
-// SIMD partner's softmax) wins when no tile needs a mask; with boundary tiles
-// the masked softmax phase becomes its long pole and the plain schedule wins
-// (measured at 75,600 tokens, 256 x 64 tiles).
+// Schedule choice: launches whose heads are all dense may take the two-group
+// schedule (one wave's MFMA work beside its SIMD partner's softmax); with
+// boundary tiles the masked softmax phase becomes its long pole and the plain
+// schedule wins.  The head_dim 128 launchers decide per tile shape (256 x 64
+// takes the plain schedule, two tiles per barrier, in every case).
+
 // Clears the work counter of the persistent schedule.  A kernel rather than a
 // memset, so that a captured graph replays it correctly.
 __global__ void clear_queue_kernel(uint32_t* q) {

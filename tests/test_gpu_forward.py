@@ -246,13 +246,15 @@ def test_dense_mask_entry_matches_coordinate_masks(sv):
         assert (bits_of(o[h]) == bits_of(o2[h])).all()
 
 
-@pytest.mark.parametrize("geom,d,bk", [((5, 24, 40), 128, 64), ((3, 5, 7), 128, 64), ((2, 9, 11), 64, 32),
-                                       ((4, 8, 8), 128, 32)])
+@pytest.mark.parametrize("geom,d,bk", [((5, 24, 40), 128, 64), ((5, 24, 40), 128, 32), ((3, 5, 7), 64, 64),
+                                       ((2, 9, 11), 64, 32), ((4, 8, 8), 128, 32)])
 def test_two_group_schedule_matches_plain_schedule(sv, geom, d, bk):
     """A launch whose heads are all dense runs the two-group schedule (block_q
-    256); the same dense head next to a spatial head runs the plain schedule.
-    Both do the same arithmetic in the same order, so the dense head's output is
-    bit-identical, and it matches the oracle.  Covers ragged q- and k-tiles."""
+    256; d128 256 x 64 launches take the plain schedule, two tiles per
+    barrier); the same dense head next to a spatial head runs the plain
+    schedule.  Both do the same arithmetic in the same order, so the dense
+    head's output is bit-identical, and it matches the oracle.  Covers ragged
+    q- and k-tiles."""
     F, H, W = geom
     heads_pp = [synth.Head("dense"), synth.Head("dense")]
     heads_plain = [synth.Head("dense"), synth.Head("spatial", window=0)]
