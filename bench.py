@@ -91,6 +91,7 @@ def main():
     ap.add_argument("--no-alt-order", action="store_true",
                     help="skip the forward with the temporal heads in the other temporal-major order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the GPU clock sample taken under load")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="forward launches timed after a 512 MB write that evicts L2 and MALL (0: skip)")
@@ -350,6 +351,12 @@ def main():
         log(f"forward after a 512 MB cache-evicting write: {cold_ms:.3f} ms")
         del flush
 
+    # ---- graphics clock under load (amd-smi, read while the forward runs back to back) ----
+    sclk = None
+    if not args.no_clock:
+        sclk = clock_under_load(lambda: layer.attend(q, k, v, out, scales))
+        log(f"graphics clock under load: {sclk}")
+
     traffic = measured_traffic(wl.name) if args.block_q == 256 and args.block_k == 64 else None
     log(f"traffic per forward launch (committed counters): {traffic}")
 
@@ -391,9 +398,51 @@ def main():
                      # HBM bytes per forward launch (FETCH_SIZE + WRITE_SIZE, calibrated), or null
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "env": {"rocm": rocm_version(), "device": torch.cuda.get_device_name(0), "sclk_under_load": sclk},
         **extra,
     }
     print(json.dumps(result), flush=True)
+
+
+def rocm_version():
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def clock_under_load(run, seconds=1.5):
+    """Graphics clock (MHz, per XCD) reported by amd-smi while `run` keeps the
+    GPU busy; None if amd-smi is unavailable.  amd-smi runs as a child process
+    and only reads the driver's clock report."""
+    import subprocess
+    import threading
+    import torch
+    found = {}
+
+    def sample():
+        time.sleep(0.5)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=30)
+            data = json.loads(r.stdout)
+            gpus = data["gpu_data"] if isinstance(data, dict) else data
+            found["mhz"] = [[v["clk"]["value"] for k, v in sorted(g["clock"].items()) if k.startswith("gfx_")]
+                            for g in gpus]
+        except Exception as e:  # amd-smi missing or its output format differs
+            found["error"] = f"{type(e).__name__}: {str(e)[:80]}"
+
+    th = threading.Thread(target=sample)
+    t_end = time.time() + seconds
+    th.start()
+    while th.is_alive() or time.time() < t_end:
+        run()
+        torch.cuda.synchronize()
+    th.join()
+    if "mhz" not in found:
+        return {"error": found.get("error")}
+    mhz = found["mhz"][0] if len(found["mhz"]) == 1 else found["mhz"]
+    return {"mhz_per_xcd": mhz, "source": "amd-smi metric -c"}
 
 
 def cpu_baseline(wl, inp, seconds):
