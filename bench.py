@@ -412,19 +412,28 @@ def rocm_version():
         return None
 
 
+AMD_SMI = "/opt/rocm/libexec/amdsmi_cli/amdsmi_cli.py"
+
+
 def clock_under_load(run, seconds=1.5):
     """Graphics clock (MHz, per XCD) reported by amd-smi while `run` keeps the
-    GPU busy; None if amd-smi is unavailable.  amd-smi runs as a child process
-    and only reads the driver's clock report."""
+    GPU busy.  amd-smi (a Python script) runs in a child interpreter started
+    directly, so no launcher re-executes anything, and it only reads the
+    driver's clock report.  Skipped under rocprofv3 (its tool library, which
+    the child would inherit, sets up the GPU in every process it is loaded
+    into) or when amd-smi is not installed."""
     import subprocess
     import threading
     import torch
+    if any(k.startswith("ROCPROF") for k in os.environ) or not os.path.exists(AMD_SMI):
+        return {"error": "skipped (running under rocprofv3, or amd-smi missing)"}
     found = {}
 
     def sample():
         time.sleep(0.5)
         try:
-            r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=30)
+            r = subprocess.run([sys.executable, AMD_SMI, "metric", "-c", "--json"], capture_output=True, text=True,
+                               timeout=30)
             data = json.loads(r.stdout)
             gpus = data["gpu_data"] if isinstance(data, dict) else data
             found["mhz"] = [[v["clk"]["value"] for k, v in sorted(g["clock"].items()) if k.startswith("gfx_")]
