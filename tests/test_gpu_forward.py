@@ -192,6 +192,27 @@ def test_edge_geometries(sv, geom, heads, bq, bk):
         assert_close(f64_of(o[h]), ref[h][0], f"edge {geom} h{h}")
 
 
+@pytest.mark.parametrize("geom,heads", [
+    ((2, 3, 5), [synth.Head("dense"), synth.Head("temporal", radius=3, order="tm")]),
+    ((5, 9, 11), [synth.Head("spatial", window=0), synth.Head("temporal", radius=1, order="tm")]),
+    ((17, 6, 8), [synth.Head("temporal", radius=2, order="tmb"), synth.Head("spatial", window=1)]),
+])
+def test_d128_two_tiles_per_barrier(sv, geom, heads):
+    """The head_dim 128, 256 x 64 launch runs two list entries between barriers.
+    These geometries give lists of 1, 3, 5, 7, 8, 12 and 13 entries (so groups
+    whose second entry is missing), ragged k- and q-tiles, patch runs shorter
+    than 16 keys (per-score test) and runs of exactly 16 in the blocked order;
+    every output row is checked against the oracle."""
+    F, H, W = geom
+    wl = synth.Workload(name="tpb", seed=79, frames=F, height=H, width=W, head_dim=128,
+                        heads=tuple(heads), tiles=((256, 64),))
+    inp = synth.make_inputs(wl)
+    o = _run_layer(sv, wl, inp, 256, 64)
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o[h]), ref[h][0], f"two tiles per barrier {geom} h{h}")
+
+
 def _bits_from_keep(keep):
     n = keep.shape[-1]
     words = (n + 31) // 32
