@@ -74,8 +74,8 @@ def measured_traffic(workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)   # >= 50 timed runs, 10 warm-up runs
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--block-q", type=int, default=256)
     ap.add_argument("--block-k", type=int, default=64)
