@@ -68,7 +68,8 @@ int check_mask(const svattn_mask* m) {
 
 bool map_bq_ok(int b) { return b == 32 || b == 64 || b == 128 || b == 256; }
 bool map_bk_ok(int b) { return b == 32 || b == 64 || b == 128; }
-bool fwd_bk_ok(int b) { return b == 32 || b == 64; }
+bool fwd_bk_ok(int b) { return b == 32 || b == 64; }                 // bit-mask entry
+bool fwd_map_bk_ok(int b) { return b == 32 || b == 64 || b == 128; }  // tile maps (128: two 64-key halves)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -329,6 +330,12 @@ static std::vector<HeadPtrs> contiguous_ptrs(int64_t n, int32_t heads, int32_t h
 
 static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int head_dim, int bq, int bk,
                         hipStream_t st) {
+  // 128-key tile maps run on the 64-key kernel, two halves per map entry
+  // (base.n_kt stays the map's k-tile count).
+  if (bk == 128) {
+    base.sub = 1;
+    bk = 64;
+  }
   for (size_t h0 = 0; h0 < descs.size(); h0 += kMaxHeadsPerLaunch) {
     FwdArgs a = base;
     const int nh = (int)std::min<size_t>(kMaxHeadsPerLaunch, descs.size() - h0);
@@ -365,8 +372,8 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
       return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] tile %d x %d differs from maps[0] %d x %d", h, m->block_q,
                   m->block_k, bq, bk);
     }
-    if (!map_bq_ok(bq) || !fwd_bk_ok(bk))
-      return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64}",
+    if (!map_bq_ok(bq) || !fwd_map_bk_ok(bk))
+      return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d: block_q in {32,64,128,256}, block_k in {32,64,128}",
                   bq, bk);
     if (m->n_qt != cdiv(n, bq) || m->n_kt != cdiv(n, bk))
       return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] dims %d x %d do not match the geometry", h, m->n_qt, m->n_kt);
@@ -516,7 +523,7 @@ int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim,
     if (!mp || !mp->row_ptr || !mp->col || !mp->col_cls) return fail(SVATTN_ERR_INVALID_ARG, "map %d incomplete", m);
     if (mp->block_q != dense_map->block_q || mp->block_k != dense_map->block_k)
       return fail(SVATTN_ERR_INVALID_ARG, "routing maps must share one tile shape");
-    if (!map_bq_ok(mp->block_q) || !fwd_bk_ok(mp->block_k))
+    if (!map_bq_ok(mp->block_q) || !fwd_map_bk_ok(mp->block_k))
       return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d", mp->block_q, mp->block_k);
     if (mp->n_qt != cdiv(n, mp->block_q) || mp->n_kt != cdiv(n, mp->block_k))
       return fail(SVATTN_ERR_INVALID_ARG, "map %d dims do not match the geometry", m);

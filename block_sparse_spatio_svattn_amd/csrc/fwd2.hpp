@@ -262,17 +262,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bool runs_ok = order != SVATTN_FRAME_MAJOR ? g.F - 1 >= 16 : g.W >= 16;
   const bool need_kc = kind == SVATTN_TEMPORAL && !runs_ok;
 
-  // Tile list: the map's CSR row; with a bit mask, every k-tile.
+  // Tile list: the map's CSR row; with a bit mask, every k-tile.  A map of
+  // (BK << sub)-key tiles is walked as 1 << sub tiles of BK keys per entry,
+  // each masked exactly on its own; the last entry's second half is dropped
+  // when it lies wholly past the last token.
+  const int sub = BITS ? 0 : a.sub;
   const int e0 = BITS ? 0 : ld_const(hd.row_ptr + qt);
-  const int n = BITS ? a.n_kt : ld_const(hd.row_ptr + qt + 1) - e0;
-
-  const int cap = a.n_qt * a.n_kt;  // capacity of col / col_cls
-  const uint8_t* __restrict__ col_cls = hd.col_cls;
   const int32_t* __restrict__ col = hd.col + e0;
+  const int n = [&]() __attribute__((always_inline)) -> int {
+    if constexpr (BITS) return a.n_kt;
+    const int len = ld_const(hd.row_ptr + qt + 1) - e0;
+    const int nn = len << sub;
+    return (sub && len > 0 && ld_const(col + len - 1) * (BK << sub) + BK >= N) ? nn - 1 : nn;
+  }();
+
+  const int cap = a.n_qt * a.n_kt;  // capacity of col / col_cls (map entries)
+  const uint8_t* __restrict__ col_cls = hd.col_cls;
   // First key of list entry j.
   auto tile_key0 = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (BITS) return j * BK;
-    else return ld_const(col + j) * BK;
+    else return ld_const(col + (j >> sub)) * (BK << sub) + (j & ((1 << sub) - 1)) * BK;
   };
   // Bit-mask rows of this lane's queries (bit j % 32 of word j / 32: pair kept).
   const uint32_t* bits_row[QG];
@@ -285,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // partial word of the buffer.
   auto tile_class = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (BITS) return SVATTN_TILE_BOUNDARY;
-    const int e = e0 + j;
+    const int e = e0 + (j >> sub);
     if ((e | 3) < cap) {
       const uint32_t w = ld_const((const uint32_t*)(col_cls + (e & ~3)));
       return (int)((w >> ((e & 3) * 8)) & 0xffu);

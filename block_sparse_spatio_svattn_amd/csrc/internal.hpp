@@ -177,6 +177,7 @@ struct FwdArgs {
   int32_t use_sel;        // 1: compute only q-tiles qt_sel[0 .. n_sel), the same for every head
   int32_t compact;        // 1: O / lse rows of selected q-tile i at i * block_q + row (with use_sel)
   int32_t qt_sel[kMaxSelectedTiles];
+  int32_t sub;            // map entries hold 1 << sub compute tiles (a 128-key map on the 64-key kernel: 1)
   int32_t dense_bits;     // 1: visit every k-tile and mask from bits
   int32_t words_per_row;  // ceil(N/32) for the bit mask
   HeadDesc heads[kMaxHeadsPerLaunch];

@@ -191,7 +191,8 @@ SVATTN_API int svattn_unpermute_order(const svattn_geom* geom, int32_t order, in
  *          of head h are in masks[h].order
  *   maps   host array [heads] of pointers to maps built for (geom, masks[h]);
  *          heads may share a map; all maps share one (block_q, block_k) with
- *          block_q in {32, 64, 128, 256} and block_k in {32, 64}; row_ptr,
+ *          block_q in {32, 64, 128, 256} and block_k in {32, 64, 128} (each
+ *          128-key tile runs as two 64-key halves, each masked exactly); row_ptr,
  *          col and col_cls must be 4-byte aligned (col_cls is read as aligned
  *          4-byte words, never past byte n_qt * n_kt - 1)
  *   scales host array [heads], finite fp32 softmax scales > 0
@@ -266,7 +267,7 @@ SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int3
  *          as for svattn_forward; the same for every head)
  *   dense_map, spatial_map, temporal_map  tile maps of the frame-major order
  *          for a DENSE mask and for spatial / temporal, one tile shape
- *          (block_q in {32, 64, 128, 256}, block_k in {32, 64})
+ *          (block_q in {32, 64, 128, 256}, block_k in {32, 64, 128})
  *   scales host fp32 [heads]
  *   qtiles host int32 [n_qtiles], 1 <= n_qtiles <= 32: distinct q-tiles, each
  *          wholly inside the sequence ((qtile + 1) * block_q <= N)

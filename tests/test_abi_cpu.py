@@ -146,7 +146,7 @@ def test_forward_validation():
     assert "overlap" in _err()
     assert _fwd(L, g, lse=FAKE * 64 + 16) == INVALID                         # lse overlaps o
     assert _fwd(L, g, maps=[_map(g, 256, 64), _map(g, 128, 64)]) == INVALID  # mixed tiles
-    assert _fwd(L, g, maps=[_map(g, 256, 128)] * 2) == UNSUPPORTED           # block_k 128
+    assert _fwd(L, g, maps=[_map(g, 256, 256)] * 2) == UNSUPPORTED           # block_k 256
     assert _fwd(L, g, maps=[_map(g, 256, 64, n_kt=5)] * 2) == INVALID
     assert _fwd(L, g, maps=[_map(g, 256, 64, col_cls=None)] * 2) == INVALID
     assert _fwd(L, g, masks=[sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR, 1, 0)] * 2) == UNSUPPORTED

@@ -213,6 +213,36 @@ def test_d128_two_tiles_per_barrier(sv, geom, heads):
         assert_close(f64_of(o[h]), ref[h][0], f"two tiles per barrier {geom} h{h}")
 
 
+@pytest.mark.parametrize("bq", [256, 128, 64])
+def test_small_128_key_tiles(sv, bq):
+    """Tile maps of 128-key tiles run as two 64-key halves per map entry.  At
+    4,800 tokens the last 128-key tile's second half lies wholly past the last
+    token and is dropped.  Every output row matches the oracle, and the output
+    is bit-identical to the one from the 64-key map (the same tiles, halves
+    without kept pairs skipped, in the same order)."""
+    wl = synth.WORKLOADS["small"]
+    assert wl.n_tokens % 128 == 64
+    inp = synth.make_inputs(wl)
+    o128 = _run_layer(sv, wl, inp, bq, 128)
+    o64 = _run_layer(sv, wl, inp, bq, 64)
+    assert (bits_of(o128) == bits_of(o64)).all()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o128[h]), ref[h][0], f"small {bq}x128 h{h}")
+
+
+def test_tiny_128_key_tiles_all_orders(sv):
+    """128-key tiles on the 256-token workload in every temporal order, against
+    the oracle."""
+    wl = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(wl)
+    for order in ("fm", "tm", "tmb"):
+        o = _run_layer(sv, wl, inp, 256, 128, orders=["fm", order])
+        ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+        for h in range(wl.n_heads):
+            assert_close(f64_of(o[h]), ref[h][0], f"tiny {order} 256x128 h{h}")
+
+
 def _bits_from_keep(keep):
     n = keep.shape[-1]
     words = (n + 31) // 32
