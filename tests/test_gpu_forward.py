@@ -543,6 +543,23 @@ def test_route_heads_closed_forms(sv):
     assert (err[:, 1] == 0).all() and (err[:, 0] > 0).all() and (ch == sv.TEMPORAL).all()
 
 
+def test_route_heads_128_key_maps(sv):
+    """Routing over 128-key tile maps (two 64-key halves per entry) gives
+    bit-identical deviations and choices to routing over 64-key maps."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    out = []
+    for bk in (64, 128):
+        g, sp, tp, dm, sm, tm = _route_setup(sv, wl, 1, 2, bq=128, bk=bk)
+        err, ch = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, [2, 17, 36])
+        torch.cuda.synchronize()
+        out.append((err.cpu().numpy(), ch.cpu().numpy()))
+    assert np.array_equal(out[0][0].view(np.uint32), out[1][0].view(np.uint32))
+    assert np.array_equal(out[0][1], out[1][1])
+
+
 @pytest.mark.parametrize("window,radius,bq", [(1, 2, 64), (0, 6, 128), (1, 12, 256)])
 def test_route_heads_against_oracle(sv, window, radius, bq):
     """Deviations within 5% of the oracle's (fp64 outputs of the same rows);
