@@ -124,6 +124,15 @@ def main():
     log(f"workload {wl.name}: N={N} heads={H} d={D} tiles {args.block_q}x{args.block_k}")
     t0 = time.time()
     inp = synth.make_inputs(wl)
+    log(f"inputs drawn on the host ({time.time() - t0:.1f} s)")
+
+    # ---- CPU oracle baseline (bounded sample), before this process touches the GPU ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        log(f"cpu oracle baseline {cpu}")
+
+    t0 = time.time()
     dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
     scales = [float(s) for s in inp.scales]
@@ -360,12 +369,6 @@ def main():
     traffic = measured_traffic(wl.name) if args.block_q == 256 and args.block_k == 64 else None
     log(f"traffic per forward launch (committed counters): {traffic}")
 
-    # ---- CPU oracle baseline (bounded sample) ----
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
-        log(f"cpu oracle baseline {cpu}")
-
     result = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -454,41 +457,105 @@ def clock_under_load(run, seconds=1.5):
     return {"mhz_per_xcd": mhz, "source": "amd-smi metric -c"}
 
 
-def cpu_baseline(wl, inp, seconds):
-    """The fp64 oracle, as it stands, on a bounded seeded sample of query rows."""
-    import numpy as np
+# Inputs of the CPU baseline's worker processes (set before the fork).
+_CPU_JOB = {}
+
+
+def _cpu_worker_init():
+    """One BLAS thread per worker process: the sample is spread over processes."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _cpu_task(task):
+    """The oracle on one block of query rows of one head; returns (head, rows, seconds)."""
     import oracle
-    import svattn_synth as synth
+    wl, inp = _CPU_JOB["wl"], _CPU_JOB["inp"]
+    h, rows = task
+    head = wl.heads[h]
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+    t = time.perf_counter()
+    oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind, head.window,
+                       head.radius, rows=rows)
+    return h, rows, time.perf_counter() - t
+
+
+def _cpu_kept(task):
+    """Kept pairs of the query rows of one block (for the FLOP count, untimed)."""
+    import oracle
+    wl = _CPU_JOB["wl"]
+    h, rows = task
+    head = wl.heads[h]
+    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+    return float(oracle.kept_counts_per_row(g, head.kind, head.window, head.radius, rows).sum())
+
+
+def _cpu_facts():
+    """Host CPU model, core counts and the BLAS numpy uses."""
+    import numpy as np
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        np.dot(np.ones((64, 64)), np.ones((64, 64)))          # loads the BLAS library
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    g = oracle.Geometry(wl.frames, wl.height, wl.width)
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas": blas}
 
-    def run(rows_per_head):
-        rows = synth.sample_rows(wl, rows_per_head)
-        fl = 0.0
-        t = time.perf_counter()
-        for h, head in enumerate(wl.heads):
-            oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), g, head.kind, head.window,
-                               head.radius, rows=rows[h])
-        dt = time.perf_counter() - t
-        for h, head in enumerate(wl.heads):
-            fl += 4 * wl.head_dim * float(oracle.kept_counts_per_row(g, head.kind, head.window, head.radius,
-                                                                     rows[h]).sum())
-        return dt, fl
 
-    rows, dt = 32, 0.0
-    while True:  # grow the sample until it costs about `seconds`
-        dt, fl = run(rows)
-        if dt >= 0.5 * seconds or rows >= 4096:
-            break
-        rows = int(min(4096, max(2 * rows, rows * 0.7 * seconds / max(dt, 1e-3))))
-    r = rows
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{r} seeded query rows per head x {wl.n_heads} heads of {wl.n_tokens}, fp64 numpy, "
-                      f"{dt:.1f} s wall", "seconds": round(dt, 2)}
+def cpu_baseline(wl, inp, seconds, max_procs=16):
+    """The fp64 oracle, as it stands, timed row-parallel on the host cores.
+
+    Worker processes (one per usable core, at most max_procs, one BLAS thread
+    each) run the oracle on blocks of seeded query rows, heads in turn, until
+    about `seconds` of wall time have passed; the value is the effective
+    FLOP of the completed rows (4 d per kept pair) over that wall time.  The
+    pool is forked before this process touches the GPU."""
+    import multiprocessing as mp
+    import svattn_synth as synth
+    facts = _cpu_facts()
+    procs = max(1, min(max_procs, facts["affinity_cores"]))
+    _CPU_JOB.update(wl=wl, inp=inp)
+    rows_all = synth.sample_rows(wl, 4096)                    # seeded, sorted per head
+    block = 64
+    tasks = [(h, rows_all[h][i:i + block]) for i in range(0, rows_all.shape[1], block) for h in range(wl.n_heads)]
+    done = []
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_task, [(0, rows_all[0][:4])] * procs)   # start-up outside the timed region
+        t0 = time.perf_counter()
+        it = iter(tasks)
+        pending = [pool.apply_async(_cpu_task, (next(it),)) for _ in range(2 * procs)]
+        while pending:
+            r = pending.pop(0).get()
+            done.append(r)
+            if time.perf_counter() - t0 < seconds:
+                nxt = next(it, None)
+                if nxt is not None:
+                    pending.append(pool.apply_async(_cpu_task, (nxt,)))
+        wall = time.perf_counter() - t0
+        kept = pool.map(_cpu_kept, [(h, rows) for h, rows, _ in done])
+    flops = 4 * wl.head_dim * float(sum(kept))
+    n_rows = sum(len(rows) for _, rows, _ in done)
+    full_rows = wl.n_heads * wl.n_tokens
+    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": procs, "kind": "oracle",
+            "sample": f"{n_rows} seeded query rows ({block}-row blocks, heads in turn) of the {wl.n_tokens}-token "
+                      f"x {wl.n_heads}-head workload, fp64 numpy oracle, {procs} processes x 1 BLAS thread, "
+                      f"{wall:.1f} s wall",
+            "seconds": round(wall, 2), "processes": procs, "blas_threads_per_process": 1, **facts,
+            "full_workload_seconds_extrapolated": round(wall * full_rows / max(n_rows, 1), 1)}
 
 
 if __name__ == "__main__":

@@ -37,7 +37,9 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SVATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-constexpr int64_t kMaxTokens = 1 << 24;
+// N < 2^23: the kernels form row byte offsets N * head_dim * 2 (< 2^31 at
+// head_dim 128) and tile indices in 32-bit arithmetic.
+constexpr int64_t kMaxTokens = (1 << 23) - 1;
 
 int check_geom(const svattn_geom* g, int64_t* n_out) {
   if (!g) return fail(SVATTN_ERR_INVALID_ARG, "geom is NULL");
@@ -45,8 +47,8 @@ int check_geom(const svattn_geom* g, int64_t* n_out) {
     return fail(SVATTN_ERR_INVALID_ARG, "geometry %d x %d x %d: every extent must be >= 1", g->frames,
                 g->height, g->width);
   const int64_t n = (int64_t)g->frames * g->height * g->width;
-  if (n > kMaxTokens) return fail(SVATTN_ERR_UNSUPPORTED, "N = %lld tokens exceeds %lld", (long long)n,
-                                  (long long)kMaxTokens);
+  if (n > kMaxTokens) return fail(SVATTN_ERR_UNSUPPORTED, "N = %lld tokens exceeds the limit %lld (N < 2^23)",
+                                  (long long)n, (long long)kMaxTokens);
   *n_out = n;
   return SVATTN_OK;
 }
@@ -377,6 +379,8 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
                   bq, bk);
     if (m->n_qt != cdiv(n, bq) || m->n_kt != cdiv(n, bk))
       return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] dims %d x %d do not match the geometry", h, m->n_qt, m->n_kt);
+    if ((int64_t)m->n_qt * m->n_kt >= (1ll << 31))
+      return fail(SVATTN_ERR_UNSUPPORTED, "maps[%d]: tile map of %d x %d blocks is too large", h, m->n_qt, m->n_kt);
     if (!m->row_ptr || !m->col || !m->col_cls) return fail(SVATTN_ERR_INVALID_ARG, "maps[%d] buffer is NULL", h);
     if (!aligned(m->row_ptr, 4) || !aligned(m->col, 4) || !aligned(m->col_cls, 4))
       return fail(SVATTN_ERR_INVALID_ARG, "maps[%d]: row_ptr, col and col_cls must be 4-byte aligned", h);
@@ -527,6 +531,8 @@ int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim,
       return fail(SVATTN_ERR_UNSUPPORTED, "forward tile %d x %d", mp->block_q, mp->block_k);
     if (mp->n_qt != cdiv(n, mp->block_q) || mp->n_kt != cdiv(n, mp->block_k))
       return fail(SVATTN_ERR_INVALID_ARG, "map %d dims do not match the geometry", m);
+    if ((int64_t)mp->n_qt * mp->n_kt >= (1ll << 31))
+      return fail(SVATTN_ERR_UNSUPPORTED, "map %d: tile map of %d x %d blocks is too large", m, mp->n_qt, mp->n_kt);
     if (!aligned(mp->row_ptr, 4) || !aligned(mp->col, 4) || !aligned(mp->col_cls, 4))
       return fail(SVATTN_ERR_INVALID_ARG, "map %d: row_ptr, col and col_cls must be 4-byte aligned", m);
   }

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
     uint32_t off = (uint32_t)dma_off[i];
     if (gathered) {  // row prow[i] of the tensor, same chunk
-      if constexpr (GTH) off = (uint32_t)(prow[i] * (D * 2) + (dma_off[i] % (D * 2)));
+      if constexpr (GTH) off = (uint32_t)prow[i] * (uint32_t)(D * 2) + (uint32_t)(dma_off[i] % (D * 2));
     } else if (ragged) {  // rows past N read row N-1 (their keys are masked)
       const int row = (int)(off / (D * 2));
       off = (uint32_t)((min(key0 + row, N - 1) - key0) * (D * 2) + (off - row * (D * 2)));

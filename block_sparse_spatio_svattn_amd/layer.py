@@ -79,8 +79,10 @@ class SparseVideoAttention:
                 permute_tokens(self.geom, src[a:b], out=dst[s:s + (b - a)], stream=stream,
                                order=self.masks[a].order)
 
-    def attend(self, q, k, v, out, scales, stream=None):
-        """Forward over all heads; temporal heads read/write the scratch buffers."""
+    def attend(self, q, k, v, out, scales, stream=None, lses=None):
+        """Forward over all heads; temporal heads read/write the scratch buffers.
+        ``lses``: optional per-head fp32 [N] tensors (or None entries) that get
+        each head's lse in that head's token order (layout positions)."""
         if self.tm_heads:
             qt, kt, vt, ot = self._buffers()
         qs, ks, vs, os_ = [], [], [], []
@@ -90,8 +92,8 @@ class SparseVideoAttention:
                 qs.append(qt[s]); ks.append(kt[s]); vs.append(vt[s]); os_.append(ot[s])
             else:
                 qs.append(q[h]); ks.append(k[h]); vs.append(v[h]); os_.append(out[h])
-        forward_ptrs(self.geom, qs, ks, vs, os_, self.masks, self.maps, scales, workspace=self.workspace,
-                     stream=stream)
+        forward_ptrs(self.geom, qs, ks, vs, os_, self.masks, self.maps, scales, lses=lses,
+                     workspace=self.workspace, stream=stream)
 
     def unpermute_output(self, out, stream=None):
         if not self.tm_heads:

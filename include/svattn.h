@@ -92,7 +92,8 @@ extern "C" {
                                        The result then depends on block_q x block_k. */
 
 typedef struct {
-  int32_t frames, height, width; /* F, H, W >= 1; N = F*H*W < 2^31 / 256 */
+  int32_t frames, height, width; /* F, H, W >= 1; N = F*H*W < 2^23 (= 2^31 / 256), else
+                                    SVATTN_ERR_UNSUPPORTED */
 } svattn_geom;
 
 typedef struct {
@@ -162,10 +163,19 @@ SVATTN_API int svattn_permutation_index_order(const svattn_geom* geom, int32_t o
                                               int32_t* inv, void* stream);
 
 /*
+ * Token reordering for temporal heads (ainews.tenesys.com, "Co się
+ * zmieniło?", item 5: temporal heads run fastest when the tokens of one
+ * patch position across frames sit next to each other, so the frame-major
+ * sequence is reordered to temporal-major before attention and back after).
  * Reorder rows of a [heads, N, head_dim] bf16 tensor frame-major ->
  * temporal-major (permute) or back (unpermute): dst[h, t', :] = src[h,
- * perm[t'], :] and its inverse.  head_dim in {64, 128}.  src and dst must not
- * overlap (no in-place).  Bit-exact row moves.
+ * perm[t'], :] and its inverse, perm as from svattn_permutation_index.
+ *   src, dst  caller-owned device buffers [heads, N, head_dim] bf16, 16-byte
+ *             aligned; they must not overlap (no in-place):
+ *             SVATTN_ERR_INVALID_ARG otherwise, or for heads < 1
+ *   head_dim  64 or 128 (SVATTN_ERR_UNSUPPORTED otherwise); heads * N *
+ *             head_dim / 8 < 2^31
+ * Bit-exact row moves, queued on `stream`.
  */
 SVATTN_API int svattn_permute_tokens(const svattn_geom* geom, int32_t heads, int32_t head_dim,
                           const void* src, void* dst, void* stream);
@@ -208,7 +218,8 @@ SVATTN_API int svattn_unpermute_order(const svattn_geom* geom, int32_t order, in
  *          the end.  The library clears the counter on `stream` before each
  *          launch; calls that can run at the same time (other streams) need
  *          distinct workspaces.  Its contents after the call are unspecified.
- * head_dim in {64, 128}.  o (and lse) must not overlap q, k or v.  The result
+ * head_dim in {64, 128}.  o (and lse) must not overlap q, k or v.  Maps with
+ * n_qt * n_kt >= 2^31 blocks are SVATTN_ERR_UNSUPPORTED.  The result
  * does not depend on the order of heads, on which heads share a map, on
  * qt_order or on the workspace: the output is bit-identical either way.
  */
@@ -289,13 +300,21 @@ SVATTN_API int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_
                                   size_t scratch_bytes, float* err, int32_t* choice, void* stream);
 
 /*
- * Reference forward for an arbitrary mask given as bits (for checking and
- * debugging; it visits every tile and masks every pair).
- *   mask_bits device uint32 [per_head ? heads : 1][n_tokens][ceil(n_tokens/32)]:
+ * Reference forward for an arbitrary mask given as bits: masked softmax
+ * attention over an explicit per-pair keep matrix (aihirek.info, section "A
+ * Sparse VideoGen a figyelmi fejeket osztályozza", paragraph 1: attention
+ * restricted to the kept query-key pairs; here the pairs are listed rather
+ * than derived from coordinates).  For checking and debugging: it visits
+ * every tile and masks every pair, so it runs at dense cost.
+ *   n_tokens  1 <= n_tokens < 2^23 (SVATTN_ERR_INVALID_ARG otherwise)
+ *   mask_bits device uint32 [per_head ? heads : 1][n_tokens][ceil(n_tokens/32)],
+ *             caller-owned, 4-byte aligned, not overlapping o:
  *             bit (j % 32) of word j / 32 of row i is 1 iff pair (i, j) is kept
  *   A query row with no kept key gets O = 0 and lse = -inf.
- * block_q in {32, 64, 128, 256}, block_k in {32, 64}; other arguments as for
- * svattn_forward.
+ * block_q in {32, 64, 128, 256}, block_k in {32, 64} (SVATTN_ERR_UNSUPPORTED
+ * otherwise); q, k, v, o, lse, scales, head_dim and stream as for
+ * svattn_forward (single token order: rows are in whatever order the bits
+ * use).
  */
 SVATTN_API int svattn_forward_dense_mask(int32_t heads, int32_t n_tokens, int32_t head_dim,
                               const uint32_t* mask_bits, int32_t per_head, const float* scales,

@@ -75,6 +75,39 @@ def _map(g, bq, bk, **kw):
     return c
 
 
+def test_token_limit_is_the_headers():
+    """N < 2^23 (the header's limit): N = 2^23 - 1 is accepted, 2^23 is not,
+    by every entry point that takes a geometry or a token count."""
+    L = sv.lib()
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    ok = sv.Geom(1, 1, (1 << 23) - 1)
+    too_big = sv.Geom(2, 1 << 11, 1 << 11)        # exactly 2^23
+    assert L.svattn_tile_map_dims(ctypes.byref(ok), 256, 64, ctypes.byref(a), ctypes.byref(b)) == OK
+    assert (a.value, b.value) == (-(-((1 << 23) - 1) // 256), -(-((1 << 23) - 1) // 64))
+    assert L.svattn_tile_map_dims(ctypes.byref(too_big), 256, 64, ctypes.byref(a), ctypes.byref(b)) == UNSUPPORTED
+    assert "2^23" in _err()
+    assert L.svattn_permute_tokens(ctypes.byref(too_big), 1, 128, FAKE, FAKE * 4, None) == UNSUPPORTED
+    assert _fwd(L, too_big) == UNSUPPORTED
+    sarr = (ctypes.c_float * 1)(0.1)
+    assert L.svattn_forward_dense_mask(1, 1 << 23, 128, FAKE, 0, sarr, FAKE, FAKE, FAKE, FAKE * 4, None, 256, 64,
+                                       None) == INVALID
+
+
+def test_forward_rejects_oversize_maps():
+    """A map of n_qt * n_kt >= 2^31 blocks (possible near the token limit with
+    32 x 32 tiles) is rejected by the forward itself, before any HIP call; the
+    kernel indexes map entries in 32-bit arithmetic."""
+    L = sv.lib()
+    g = sv.Geom(4, 1024, 2000)                     # N = 8,192,000 < 2^23
+    big = _map(g, 32, 32)
+    assert big.n_qt * big.n_kt >= 1 << 31
+    masks = [sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, 1, 0)]
+    assert _fwd(L, g, heads=1, masks=masks, maps=[big], q=FAKE, k=FAKE << 8, v=FAKE << 9, o=FAKE << 10) == UNSUPPORTED
+    assert "too large" in _err()
+    mask = sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, 1, 0)
+    assert L.svattn_build_tile_map_ex(ctypes.byref(g), ctypes.byref(mask), ctypes.byref(big), 0, None) == UNSUPPORTED
+
+
 def test_build_tile_map_validation():
     L = sv.lib()
     g = sv.Geom(5, 24, 40)

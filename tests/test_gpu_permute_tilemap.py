@@ -130,6 +130,41 @@ def test_tile_map_large_sampled_rows(sv, wl_name, hi, order, bq, bk):
     _compare_map(m, ref, qtiles)
 
 
+def _oracle_map_threaded(geom, kind, w, r, order, bq, bk):
+    """oracle.tile_map over every q-tile row, one row per task on a thread pool
+    (numpy releases the GIL in its array loops); rows assembled in order, so the
+    result is the same as oracle.tile_map over all rows."""
+    from concurrent.futures import ThreadPoolExecutor
+    g = oracle.Geometry(*geom)
+    n_qt = -(-g.n // bq)
+
+    def one(qt):
+        return oracle.tile_map(g, kind, w, r, order, bq, bk, qtiles=[qt])
+    with ThreadPoolExecutor(16) as ex:
+        rows = list(ex.map(one, range(n_qt)))
+    cls = np.concatenate([x[0] for x in rows])
+    lens = np.array([x[1][1] for x in rows], dtype=np.int64)
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    col = np.concatenate([x[2] for x in rows]).astype(np.int32)
+    col_cls = np.concatenate([x[3] for x in rows]).astype(np.uint8)
+    return cls, row_ptr, col, col_cls
+
+
+@pytest.mark.parametrize("wl_name,hi,order", [("headline", 0, "fm"), ("headline", 5, "tm"),
+                                              ("headline", 5, "tmb"), ("perm_study", 0, "tmb")])
+def test_tile_map_full_size_every_row(sv, wl_name, hi, order):
+    """The benchmark's 256 x 64 maps at 75,600 tokens, whole: every q-tile row's
+    classes, CSR list and the longest-first q-tile order, bit for bit."""
+    wl = synth.WORKLOADS[wl_name]
+    h = wl.heads[hi]
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    print(f"full map {wl_name} head {hi} ({h.kind}) order {order}", flush=True)
+    m = sv.build_tile_map(g, sv_mask(h, order), 256, 64)
+    torch.cuda.synchronize()
+    ref = _oracle_map_threaded((wl.frames, wl.height, wl.width), h.kind, h.window, h.radius, order, 256, 64)
+    _compare_map(m, ref)
+
+
 def test_all_boundary_flag(sv):
     g = sv.Geom(5, 24, 40)
     mk = sv_mask(synth.Head("temporal", radius=2, order="tm"))

@@ -80,3 +80,46 @@ def test_tile_classes_match_oracle(exe, geom, kind, w, r, order, bq, bk):
     ref, *_ = oracle.tile_map(oracle.Geometry(F, H, W), kind, w, r, order, bq, bk)
     assert got.shape == ref.shape
     assert (got == ref).all()
+
+
+# ---- full-size maps: every q-tile row of the 75,600-token maps, a stratified
+# set of rows of the 302,400-token maps (256 x 64 tiles, the benchmark's) ----
+
+def _oracle_rows_threaded(g, kind, w, r, order, bq, bk, rows):
+    """oracle.tile_map row by row on a thread pool (numpy releases the GIL in
+    its array loops, so the brute force runs on every core)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(qt):
+        return oracle.tile_map(g, kind, w, r, order, bq, bk, qtiles=[qt])[0][0]
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        return np.stack(list(ex.map(one, rows)))
+
+
+FULL_SIZE_MAPS = [
+    ((21, 45, 80), "spatial", 1, 0, "fm", None),
+    ((21, 45, 80), "temporal", 0, 31, "tm", None),
+    ((21, 45, 80), "temporal", 0, 31, "tmb", None),
+    ((21, 45, 80), "temporal", 0, 22, "tmb", None),
+    ((21, 90, 160), "spatial", 1, 0, "fm", 16),
+    ((21, 90, 160), "temporal", 0, 62, "tmb", 16),
+]
+
+
+@pytest.mark.parametrize("geom,kind,w,r,order,stride", FULL_SIZE_MAPS)
+def test_full_size_tile_classes_match_oracle(exe, geom, kind, w, r, order, stride):
+    """Host build of the classifier vs the brute-force oracle on full-size
+    maps.  stride None: every q-tile row; else rows 0, 1, the last two (the
+    last one ragged when block_q does not divide N) and every stride-th row."""
+    F, H, W = geom
+    bq, bk = 256, 64
+    g = oracle.Geometry(F, H, W)
+    n_qt = -(-g.n // bq)
+    out = [row for row in _run(exe, F, H, W, ORDERS[order], KINDS[kind], w, r, bq, bk) if row]
+    assert len(out) == n_qt
+    rows = list(range(n_qt)) if stride is None else sorted({0, 1, n_qt - 2, n_qt - 1, *range(0, n_qt, stride)})
+    got = np.array([[int(c) for c in out[qt]] for qt in rows], dtype=np.uint8)
+    ref = _oracle_rows_threaded(g, kind, w, r, order, bq, bk, rows)
+    assert got.shape == ref.shape
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} blocks differ, first at q-tile row {rows[bad[0][0]]}, k-tile {bad[0][1]}"
