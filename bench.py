@@ -528,7 +528,7 @@ def cpu_baseline(wl, inp, seconds, max_procs=16):
     facts = _cpu_facts()
     procs = max(1, min(max_procs, facts["affinity_cores"]))
     _CPU_JOB.update(wl=wl, inp=inp)
-    rows_all = synth.sample_rows(wl, 4096)                    # seeded, sorted per head
+    rows_all = synth.sample_rows(wl, min(wl.n_tokens, 32768))  # seeded, sorted per head; time-bounded below
     block = 64
     tasks = [(h, rows_all[h][i:i + block]) for i in range(0, rows_all.shape[1], block) for h in range(wl.n_heads)]
     done = []

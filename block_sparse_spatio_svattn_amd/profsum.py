@@ -19,7 +19,7 @@ import json
 import statistics
 from collections import OrderedDict
 
-BF16_PEAK_TFLOPS = 2516.6
+BF16_PEAK_TFLOPS = 2500.0  # published dense bf16 MFMA peak of MI355X
 
 
 def load(path):
