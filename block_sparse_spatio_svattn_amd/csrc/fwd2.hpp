@@ -430,6 +430,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // keep mask of its query over the tile's keys from ranges and runs, then
   // applies it with one bit extract and one bit select per score.
   auto apply_keep = [&](int gq, uint64_t m, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
+    const uint32_t ninf = 0xff800000u;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
       const uint32_t w = (uint32_t)(m >> (32 * kb)) >> (4 * hh);
@@ -437,23 +438,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int i = 0; i < 16; ++i) {
         const int pos = 8 * (i / 4) + (i % 4);
         const uint32_t t = (uint32_t)((int)(w << (31 - pos)) >> 31);  // all ones iff kept
-        // (a bit cast straight from a vector element reads element 0 with this
-        // compiler, so the score goes through a scalar first)
-        const float sf = S[kb][gq][i];
-        const uint32_t sb = __builtin_bit_cast(uint32_t, sf);
-        S[kb][gq][i] = __builtin_bit_cast(float, (sb & t) | (0xff800000u & ~t));  // else -inf
+        // score = t ? score : -inf, written over the score in place (the
+        // output is tied to the input), so masked and unmasked tiles leave
+        // the scores in the same registers and nothing is copied where the
+        // two paths meet.  (A bit cast straight from a vector element reads
+        // element 0 with this compiler, so the score goes through a scalar.)
+        float sf = S[kb][gq][i];
+        asm("v_bfi_b32 %0, %1, %0, %2" : "+v"(sf) : "v"(t), "s"(ninf));
+        S[kb][gq][i] = sf;
       }
     }
   };
   constexpr int MAXR = BK / 16 + 1;  // runs of >= 16 keys in one tile
-  // Mask plan of the tile starting at key0, from coordinates only (so it can
-  // run before the tile's scores exist).  Returns, the same for the whole
-  // wave: 1 if no score needs masking (not a boundary or ragged tile, or every
-  // pair kept), 2 if every score of the wave's queries is masked (the tile
-  // changes nothing for them: S, softmax and P V are skipped), 0 if the keep
-  // masks in keep[] must be applied, 3 if the per-score test (bit-mask input,
-  // or temporal heads with short key runs) must run on the scores.
-  auto plan = [&](int key0, int cls, uint64_t (&keep)[QG]) __attribute__((always_inline)) -> int {
+  // Mask plan of the tile starting at key0 (in stage st), from coordinates or
+  // mask bits only, so it runs before the tile's scores exist.  Returns, the
+  // same for the whole wave: 1 if no score needs masking (not a boundary or
+  // ragged tile, or every pair kept), 2 if every score of the wave's queries
+  // is masked (the tile changes nothing for them: S, softmax and P V are
+  // skipped), 0 if the per-lane keep masks in keep[] (bit kk: key key0 + kk of
+  // the lane's query is kept) must be applied.
+  auto plan = [&](int st, int key0, int cls, uint64_t (&keep)[QG]) __attribute__((always_inline)) -> int {
     if (!(cls == SVATTN_TILE_BOUNDARY || key0 + BK > N)) return 1;
     const int lim_anchor = g.P - key0;    // kk < lim_anchor: frame-0 key
     const int lim_n = N - key0;           // kk >= lim_n: past the last token
@@ -461,12 +465,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // only the key range applies (with tile-aligned maps it keeps pairs the
     // coordinate mask would drop).
     const int mkind = cls == SVATTN_TILE_BOUNDARY ? kind : SVATTN_DENSE;
-    if constexpr (BITS) return 3;
-    if (mkind == SVATTN_TEMPORAL && !runs_ok) return 3;
     {
       const uint64_t in_range = bit_range(0, lim_n);
       const uint64_t anchor = bit_range(0, lim_anchor);
-      if (mkind == SVATTN_SPATIAL) {
+      if constexpr (BITS) {
+        // the lane's row of the bit mask: one 32-bit word per 32 keys
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+          const uint32_t w0 = bits_row[gq][key0 >> 5];
+          const uint32_t w1 = (BK > 32 && lim_n > 32) ? bits_row[gq][(key0 >> 5) + 1] : 0u;
+          keep[gq] = ((uint64_t)w1 << 32) | w0;
+        }
+      } else if (mkind == SVATTN_TEMPORAL && !runs_ok) {
+        // short key runs: the lane's own keys tested one by one against the
+        // per-key patch coordinates the copier waves wrote to LDS
+        const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) keep[gq] = anchor;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int kk0 = kb * 32 + 8 * i4 + 4 * hh;
+            const int4 kc4 = *(const int4*)&kcs[st][kk0];
+            const int kcv[4] = {kc4.x, kc4.y, kc4.z, kc4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int yk = kcv[j] >> 16, xk = kcv[j] & 0xffff;
+#pragma unroll
+              for (int gq = 0; gq < QG; ++gq) {
+                const bool ok = ((uint32_t)(yk - mq_a[gq]) + r <= r2) & ((uint32_t)(xk - mq_b[gq]) + r <= r2);
+                keep[gq] |= (uint64_t)ok << (kk0 + j);
+              }
+            }
+          }
+        }
+      } else if (mkind == SVATTN_SPATIAL) {
         // kept non-anchor keys: [mq_a, mq_a + mq_b)
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) keep[gq] = bit_range(mq_a[gq] - key0, mq_a[gq] + mq_b[gq] - key0) | anchor;
@@ -566,58 +600,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
 
-  // Per-score test of a boundary tile (plan() returned 3).
-  auto mask_scores = [&](int st, int key0, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) {
-    const int lim_anchor = g.P - key0;
-    const int lim_n = N - key0;
-    const int lane_kk = 4 * hh;
-    if constexpr (BITS) {
-#pragma unroll
-      for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          const uint32_t word = kb * 32 < lim_n ? bits_row[gq][(key0 >> 5) + kb] : 0u;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = kb * 32 + 8 * (i / 4) + (i % 4) + lane_kk;
-            const bool keep = ((word >> (kk & 31)) & 1u) & (kk < lim_n);
-            S[kb][gq][i] = keep ? S[kb][gq][i] : -INFINITY;
-          }
-        }
-    } else {
-      // short runs: per-key patch coordinates from LDS
-      const uint32_t r = (uint32_t)hd.radius, r2 = 2u * r;
-      const bool any_anchor = lim_anchor > 0;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int kk0 = kb * 32 + 8 * i4 + lane_kk;
-          const int4 kc4 = *(const int4*)&kcs[st][kk0];
-          const int kcv[4] = {kc4.x, kc4.y, kc4.z, kc4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int yk = kcv[j] >> 16, xk = kcv[j] & 0xffff;
-            const bool anchor = any_anchor & (kk0 + j < lim_anchor);
-#pragma unroll
-            for (int gq = 0; gq < QG; ++gq) {
-              const bool keep = (((uint32_t)(yk - mq_a[gq]) + r <= r2) & ((uint32_t)(xk - mq_b[gq]) + r <= r2)) | anchor;
-              S[kb][gq][i4 * 4 + j] = keep ? S[kb][gq][i4 * 4 + j] : -INFINITY;
-            }
-          }
-        }
-      }
-    }
-  };
-  // plan + apply in one step (the two-group schedule).
+  // plan + apply in one step (the two-group schedule): masked scores become
+  // -inf before the softmax.
   auto mask = [&](int st, int key0, int cls, floatx16 (&S)[C::KB][QG]) __attribute__((always_inline)) -> int {
     uint64_t keep[QG];
-    const int m = plan(key0, cls, keep);
-    if (m == 0) {
+    const int m = plan(st, key0, cls, keep);
+    if (m != 1) {
 #pragma unroll
-      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
-    } else if (m == 3) {
-      mask_scores(st, key0, S);
+      for (int gq = 0; gq < QG; ++gq) apply_keep(gq, m == 2 ? 0ull : keep[gq], S);
     }
     return m;
   };
@@ -823,14 +813,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             if (gathered && t + 1 < n) gather_rows(wk[1]);
           // a wave whose queries keep no key of this tile skips S, softmax and P V
           uint64_t keep[QG];
-          const int ms = plan(wk[0], wc[0], keep);
+          const int ms = plan(st, wk[0], wc[0], keep);
           if (ms != 2) {
             qk(st, S, [](int) {});
             if (ms == 0) {
 #pragma unroll
               for (int gq = 0; gq < QG; ++gq) apply_keep(gq, keep[gq], S);
-            } else if (ms == 3) {
-              mask_scores(st, wk[0], S);
             }
             softmax(S, P, [](int) {});
           }
