@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.svattn_unpermute_order.argtypes = [P(Geom), _i32, _i32, _i32, _vp, _vp, _vp]
     L.svattn_forward.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.svattn_forward_noalloc.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
+                                         _vp, _vp, _vp, _vp, _vp, _vp]
     L.svattn_forward_ptrs.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
                                       P(_vp), P(_vp), P(_vp), P(_vp), P(_vp), _vp, _vp]
     L.svattn_forward_fused.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
@@ -115,6 +117,7 @@ def lib() -> ctypes.CDLL:
               "svattn_permutation_index", "svattn_permute_tokens", "svattn_unpermute",
               "svattn_permutation_index_order", "svattn_permute_tokens_order", "svattn_unpermute_order",
               "svattn_forward", "svattn_forward_ptrs", "svattn_forward_fused", "svattn_forward_dense_mask",
+              "svattn_forward_noalloc",
               "svattn_route_scratch_bytes", "svattn_route_heads"):
         getattr(L, f).restype = ctypes.c_int
     _LIB = L
@@ -308,6 +311,27 @@ def forward_fused(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       perm_p, _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
                                       _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
                                       lse_p, _ws(workspace), _stream(stream)), "svattn_forward_fused")
+    return out
+
+
+def forward_noalloc(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    masks: Sequence[Mask], maps: Sequence[TileMap], scales: Sequence[float],
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """svattn_forward_noalloc: the persistent forward with the library's own
+    per-device work counter (no workspace).  Calls on one GPU must not overlap."""
+    heads = q.shape[0]
+    out = _qkvo(q, k, v, out, geom.n)
+    if len(masks) != heads or len(maps) != heads:
+        raise SvattnError("need one mask and one map per head")
+    marr = (Mask * heads)(*[Mask(m.kind, m.order, m.window, m.radius) for m in masks])
+    P = ctypes.POINTER(_TileMapC)
+    parr = (P * heads)(*[ctypes.pointer(m.c) for m in maps])
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check(lib().svattn_forward_noalloc(ctypes.byref(geom), heads, q.shape[-1], marr, parr, _scales(scales, heads),
+                                        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                                        _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
+                                        lse_p, _stream(stream)), "svattn_forward_noalloc")
     return out
 
 

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "internal.hpp"
@@ -114,6 +115,34 @@ int check_map_buffers(const svattn_tile_map* map, const char* who) {
 // memset, so that a captured graph replays it correctly.
 __global__ void clear_queue_kernel(uint32_t* q) {
   if (threadIdx.x == 0) q[0] = 0u;
+}
+
+// Work counter area of svattn_forward_noalloc, for callers that cannot
+// allocate a workspace.  One copy per GPU, held until the process ends.  In
+// host code this name only stands in for the symbol: kernels get the device
+// address that noalloc_scratch() looks up once per device.
+static __device__ __align__(256) uint32_t scratch[kNoallocScratchBytes / 4];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, then cached).
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SVATTN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SVATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVATTN_OK;
 }
 
 hipError_t dispatch_forward(const FwdArgs& a, int head_dim, int bq, int bk, hipStream_t st) {
@@ -356,10 +385,13 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
   return SVATTN_OK;
 }
 
+// use_scratch: the work counter lives in the library's per-device `scratch`
+// (svattn_forward_noalloc) instead of the caller's workspace; it is looked up
+// after every argument check, so validation still precedes any HIP call.
 static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32_t head_dim,
                         const svattn_mask* masks, const svattn_tile_map* const* maps, const float* scales,
                         const std::vector<HeadPtrs>& ptrs, void* workspace, void* stream,
-                        const int32_t* perm = nullptr) {
+                        const int32_t* perm = nullptr, bool use_scratch = false) {
   int s;
   if (!masks || !maps) return fail(SVATTN_ERR_INVALID_ARG, "masks / maps is NULL");
   int bq = 0, bk = 0;
@@ -429,6 +461,11 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
   a.chunk = 32;
   a.dense_bits = 0;
   a.queue = (uint32_t*)workspace;
+  if (use_scratch) {
+    void* p = nullptr;
+    if ((s = noalloc_scratch(&p))) return s;
+    a.queue = (uint32_t*)p;
+  }
   return run_launches(a, sorted, head_dim, bq, bk, (hipStream_t)stream);
 }
 
@@ -442,6 +479,18 @@ int svattn_forward(const svattn_geom* geom, int32_t heads, int32_t head_dim, con
   if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
   return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
                       contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream);
+}
+
+int svattn_forward_noalloc(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
+                           const svattn_tile_map* const* maps, const float* scales, const void* q, const void* k,
+                           const void* v, void* o, float* lse, void* stream) {
+  int64_t n;
+  int s = check_geom(geom, &n);
+  if (s) return s;
+  if ((s = check_common(heads, head_dim, scales))) return s;
+  if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
+  return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
+                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), nullptr, stream, nullptr, true);
 }
 
 int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,

@@ -162,6 +162,10 @@ struct HeadDesc {
 };
 
 constexpr int kMaxHeadsPerLaunch = 16;
+// Size of the library-held work-counter area of svattn_forward_noalloc (one
+// copy per device): the forward needs SVATTN_FORWARD_WORKSPACE_BYTES.
+constexpr int kNoallocScratchBytes = 256;
+static_assert(kNoallocScratchBytes >= SVATTN_FORWARD_WORKSPACE_BYTES, "forward workspace must fit the scratch area");
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSelectedTiles = 32;  // q-tiles of a selected-rows launch (kernel arguments)
 constexpr float kLog2eHost = 1.4426950408889634f;

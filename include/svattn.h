@@ -229,6 +229,27 @@ SVATTN_API int svattn_forward(const svattn_geom* geom, int32_t heads, int32_t he
                               void* o, float* lse, void* workspace, void* stream);
 
 /*
+ * svattn_forward with the persistent schedule and no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The work counter
+ * lives in a 256-byte area the library holds in device memory, one copy per
+ * GPU for the life of the process; the call allocates nothing.  The area's
+ * device address is looked up on the first call on each device (a HIP call
+ * made after every argument check).  Its size does not depend on the
+ * arguments, so no size is rejected for it; the other limits are those of
+ * svattn_forward.  Every call on one GPU shares that area: calls that can
+ * overlap on one GPU (different streams, or graph replays that overlap) race
+ * on it and must not be issued; calls queued on one stream are safe (the
+ * counter is cleared by a kernel before each launch).  Arguments, layouts,
+ * errors and results as for svattn_forward (bit-identical to it with a
+ * workspace).
+ */
+SVATTN_API int svattn_forward_noalloc(const svattn_geom* geom, int32_t heads, int32_t head_dim,
+                                      const svattn_mask* masks, const svattn_tile_map* const* maps,
+                                      const float* scales, const void* q, const void* k, const void* v,
+                                      void* o, float* lse, void* stream);
+
+/*
  * Same as svattn_forward, with a separate device pointer per head instead of
  * one [heads, N, head_dim] tensor: q[h], k[h], v[h], o[h] are [N, head_dim]
  * bf16 (16-byte aligned), lse is NULL or a host array whose entries are NULL

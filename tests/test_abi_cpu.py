@@ -225,6 +225,16 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 256, 64, dtype=torch.bfloat16)
     with pytest.raises(sv.SvattnError):
         sv.permute_tokens(g, x, out=torch.zeros_like(x))
+    # the forward bindings marshal their arguments, then refuse host tensors
+    # before calling the library
+    from types import SimpleNamespace
+    mp = SimpleNamespace(c=_map(g, 256, 64))
+    masks = [sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, 1, 0)]
+    for fn in (sv.forward, sv.forward_noalloc):
+        with pytest.raises(sv.SvattnError, match="CUDA \\(HIP\\) tensor"):
+            fn(g, x, x, x, masks, [mp], [0.125])
+        with pytest.raises(sv.SvattnError, match="one mask and one map per head"):
+            fn(g, x, x, x, masks * 2, [mp], [0.125])
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device error path")
