@@ -2,6 +2,7 @@
 
     python -m block_sparse_spatio_svattn_amd.profsum TRACE.csv [--kernel fwd2_kernel]
         [--skip W] [--flop F] [--bench-line BENCH.json]
+    python -m block_sparse_spatio_svattn_amd.profsum --counters COUNTERS.csv [...] [--kernel NAME]
 
 Prints a markdown table of every kernel (calls, mean / median / min / max
 duration) and, for the kernel whose name contains ``--kernel``, the same
@@ -9,7 +10,9 @@ figures over its dispatches after the first ``--skip`` (the bench's warm-up
 calls), so the trace can be checked against the bench line of the same run:
 with ``--flop`` (algorithmic FLOP per dispatch) it adds the effective TFLOP/s
 and the fraction of the bf16 dense MFMA peak, and with ``--bench-line`` it
-prints that line's forward time and roofline fraction beside them.
+prints that line's forward time and roofline fraction beside them.  With
+``--counters`` it reads rocprofv3 --pmc counter_collection.csv files instead
+and prints each counter's mean per dispatch of the named kernel.
 """
 from __future__ import annotations
 
@@ -38,7 +41,37 @@ def stats_us(durs_ns):
             "min_us": min(d), "max_us": max(d), "total_us": sum(d)}
 
 
+def load_counters(path, kernel):
+    """{counter: [value per dispatch]} for the dispatches of kernels whose name
+    contains `kernel`, from a rocprofv3 --pmc counter_collection.csv."""
+    per = OrderedDict()
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], OrderedDict()).setdefault(int(r["Dispatch_Id"]), 0.0)
+                per[r["Counter_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def counters_main(argv):
+    """--counters CSV [CSV ...] --kernel NAME: per-dispatch mean of every
+    counter of the named kernel (one JSON object)."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--counters", nargs="+", required=True)
+    ap.add_argument("--kernel", default="fwd2_kernel")
+    a = ap.parse_args(argv)
+    out = {}
+    for path in a.counters:
+        for name, vals in load_counters(path, a.kernel).items():
+            out[name] = {"dispatches": len(vals), "mean": statistics.fmean(vals)}
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
+    import sys
+    argv = sys.argv[1:] if argv is None else argv
+    if argv and argv[0] == "--counters":
+        return counters_main(argv)
     ap = argparse.ArgumentParser()
     ap.add_argument("trace")
     ap.add_argument("--kernel", default="fwd2_kernel")
