@@ -372,7 +372,8 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
     const int nh = (int)std::min<size_t>(kMaxHeadsPerLaunch, descs.size() - h0);
     for (int i = 0; i < nh; ++i) a.heads[i] = descs[h0 + i];
     a.n_slots = nh;
-    a.n_items = nh * a.n_sel;
+    if (a.n_split < 1) a.n_split = 1;
+    a.n_items = nh * a.n_sel * a.n_split;
     if (a.queue) {
       // launches on one stream run in order, so one counter serves them all
       hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, st, a.queue);
@@ -536,23 +537,45 @@ int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_di
                       contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream, any_tm ? perm : nullptr);
 }
 
-static int route_dims(int32_t heads, int32_t head_dim, int32_t block_q, int32_t n_qtiles, size_t* part) {
+// Key splits per (head, q-tile) of a routing launch: enough work items (three
+// masks * heads * q-tiles * splits) for about four per compute unit of a
+// 256-unit chip, at most 32.
+static int route_splits(int32_t heads, int32_t n_qtiles) {
+  const int64_t per = 3ll * heads * n_qtiles;
+  return (int)std::min<int64_t>(32, std::max<int64_t>(1, (1024 + per - 1) / per));
+}
+
+// Routing scratch: the forward's work counter, then per mask (dense, spatial,
+// temporal) the split partial outputs (fp32 rows) and their lse, then the
+// per-workgroup deviation sums.
+struct RouteLayout {
+  int n_split;
+  size_t o_bytes, lse_bytes, perr_off, total;  // o_bytes, lse_bytes: one mask
+};
+
+static int route_dims(int32_t heads, int32_t head_dim, int32_t block_q, int32_t n_qtiles, RouteLayout* lay) {
   if (heads < 1 || heads > (1 << 16)) return fail(SVATTN_ERR_INVALID_ARG, "heads = %d", heads);
   if (head_dim != 64 && head_dim != 128) return fail(SVATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
   if (!map_bq_ok(block_q)) return fail(SVATTN_ERR_UNSUPPORTED, "block_q %d not in {32, 64, 128, 256}", block_q);
   if (n_qtiles < 1 || n_qtiles > kMaxSelectedTiles)
     return fail(SVATTN_ERR_INVALID_ARG, "n_qtiles = %d must be in [1, %d]", n_qtiles, kMaxSelectedTiles);
-  *part = (size_t)heads * n_qtiles * block_q * head_dim * 2;  // one compact output
+  lay->n_split = route_splits(heads, n_qtiles);
+  const size_t rows = (size_t)heads * n_qtiles * lay->n_split * block_q;
+  lay->o_bytes = rows * head_dim * 4;
+  lay->lse_bytes = rows * 4;
+  lay->perr_off = SVATTN_FORWARD_WORKSPACE_BYTES + 3 * (lay->o_bytes + lay->lse_bytes);
+  const size_t blocks = (size_t)heads * n_qtiles * (block_q / route_rows_per_block(head_dim));
+  lay->total = lay->perr_off + blocks * 2 * 4;
   return SVATTN_OK;
 }
 
 int svattn_route_scratch_bytes(int32_t heads, int32_t head_dim, int32_t block_q, int32_t n_qtiles,
                                size_t* bytes) {
-  size_t part;
-  int s = route_dims(heads, head_dim, block_q, n_qtiles, &part);
+  RouteLayout lay;
+  int s = route_dims(heads, head_dim, block_q, n_qtiles, &lay);
   if (s) return s;
   if (!bytes) return fail(SVATTN_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = 3 * part;
+  *bytes = lay.total;
   return SVATTN_OK;
 }
 
@@ -586,8 +609,8 @@ int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim,
       return fail(SVATTN_ERR_INVALID_ARG, "map %d: row_ptr, col and col_cls must be 4-byte aligned", m);
   }
   const int bq = dense_map->block_q, bk = dense_map->block_k;
-  size_t part;
-  if ((s = route_dims(heads, head_dim, bq, n_qtiles, &part))) return s;
+  RouteLayout lay;
+  if ((s = route_dims(heads, head_dim, bq, n_qtiles, &lay))) return s;
   if (!qtiles) return fail(SVATTN_ERR_INVALID_ARG, "qtiles is NULL");
   for (int i = 0; i < n_qtiles; ++i) {
     if (qtiles[i] < 0 || (int64_t)(qtiles[i] + 1) * bq > n)
@@ -600,38 +623,54 @@ int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(scratch, 16) || !aligned(err, 4) ||
       !aligned(choice, 4))
     return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / scratch need 16-byte, err / choice 4-byte alignment");
-  if (scratch_bytes < 3 * part)
-    return fail(SVATTN_ERR_INVALID_ARG, "scratch of %zu bytes, %zu needed", scratch_bytes, 3 * part);
+  if (scratch_bytes < lay.total)
+    return fail(SVATTN_ERR_INVALID_ARG, "scratch of %zu bytes, %zu needed", scratch_bytes, lay.total);
   const size_t tb = (size_t)heads * n * head_dim * 2, eb = (size_t)heads * 8, cb = (size_t)heads * 4;
   const void* ins[3] = {q, k, v};
   for (const void* in : ins)
-    if (overlap(scratch, 3 * part, in, tb) || overlap(err, eb, in, tb) || overlap(choice, cb, in, tb))
+    if (overlap(scratch, lay.total, in, tb) || overlap(err, eb, in, tb) || overlap(choice, cb, in, tb))
       return fail(SVATTN_ERR_INVALID_ARG, "scratch / err / choice overlap q, k or v");
-  if (overlap(err, eb, scratch, 3 * part) || overlap(choice, cb, scratch, 3 * part) || overlap(err, eb, choice, cb))
+  if (overlap(err, eb, scratch, lay.total) || overlap(choice, cb, scratch, lay.total) || overlap(err, eb, choice, cb))
     return fail(SVATTN_ERR_INVALID_ARG, "scratch, err and choice must not overlap");
 
+  // One forward over the sampled q-tiles of all three masks: work items are
+  // (mask, head, q-tile, key split), the dense and temporal ones (long rows)
+  // first, taken from a shared counter.
+  char* sc = (char*)scratch;
+  const float* o_part[3];
+  const float* lse_part[3];
   FwdArgs base;
   memset(&base, 0, sizeof(base));
   base.g = make_geo(*geom);
   base.n_qt = (int32_t)cdiv(n, bq);
   base.n_kt = (int32_t)cdiv(n, bk);
   base.chunk = 32;
+  base.queue = (uint32_t*)sc;
   base.use_sel = 1;
   base.compact = 1;
+  base.partial = 1;
+  base.n_split = lay.n_split;
   base.n_sel = n_qtiles;
   for (int i = 0; i < n_qtiles; ++i) base.qt_sel[i] = qtiles[i];
   const svattn_mask dense{SVATTN_DENSE, SVATTN_FRAME_MAJOR, 0, 0};
   const svattn_mask* masks3[3] = {&dense, spatial, temporal};
-  const size_t hb = (size_t)n * head_dim * 2, ob = (size_t)n_qtiles * bq * head_dim * 2;
-  for (int m = 0; m < 3; ++m) {
-    std::vector<HeadDesc> descs(heads);
+  const size_t rows_h = (size_t)n_qtiles * lay.n_split * bq;  // partial rows of one head
+  std::vector<HeadDesc> descs;
+  descs.reserve(3 * (size_t)heads);
+  for (int m : {0, 2, 1}) {
+    float* o_m = (float*)(sc + SVATTN_FORWARD_WORKSPACE_BYTES + m * lay.o_bytes);
+    float* l_m = (float*)(sc + SVATTN_FORWARD_WORKSPACE_BYTES + 3 * lay.o_bytes + m * lay.lse_bytes);
+    o_part[m] = o_m;
+    lse_part[m] = l_m;
     for (int h = 0; h < heads; ++h) {
-      HeadDesc& d = descs[h];
+      HeadDesc d;
       memset(&d, 0, sizeof(d));
+      const size_t hb = (size_t)n * head_dim * 2;
       d.q = (const char*)q + h * hb;
       d.k = (const char*)k + h * hb;
       d.v = (const char*)v + h * hb;
-      d.o = (char*)scratch + m * part + h * ob;
+      d.o = o_m + h * rows_h * head_dim;
+      d.lse = l_m + h * rows_h;
       d.row_ptr = maps3[m]->row_ptr;
       d.col = maps3[m]->col;
       d.col_cls = maps3[m]->col_cls;
@@ -641,11 +680,12 @@ int svattn_route_heads(const svattn_geom* geom, int32_t heads, int32_t head_dim,
       d.order = SVATTN_FRAME_MAJOR;
       d.window = masks3[m]->window;
       d.radius = masks3[m]->radius;
+      descs.push_back(d);
     }
-    if ((s = run_launches(base, descs, head_dim, bq, bk, (hipStream_t)stream))) return s;
   }
-  hipError_t e = launch_route(scratch, (const char*)scratch + part, (const char*)scratch + 2 * part, heads,
-                              (int64_t)(ob / 2), (int64_t)(ob / 2), err, choice, (hipStream_t)stream);
+  if ((s = run_launches(base, descs, head_dim, bq, bk, (hipStream_t)stream))) return s;
+  hipError_t e = launch_route(o_part, lse_part, heads, n_qtiles, lay.n_split, bq, head_dim,
+                              (float*)(sc + lay.perr_off), err, choice, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "routing launch");
   return SVATTN_OK;
 }

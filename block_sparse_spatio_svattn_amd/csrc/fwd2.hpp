@@ -61,6 +61,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 template <int D, int BK, int NW, int QG>
@@ -180,8 +181,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     item = __builtin_amdgcn_readfirstlane(ticket);
   }
   while (item < a.n_items) {
-  const int slot = item / a.n_sel;
-  const int sel = item - slot * a.n_sel;  // rank of the q-tile among the head's work items
+  const int per_slot = a.n_sel * a.n_split;
+  const int slot = item / per_slot;
+  const int rest = item - slot * per_slot;
+  const int sel = a.n_split == 1 ? rest : rest / a.n_split;  // rank of the q-tile among the head's work items
+  const int split = rest - sel * a.n_split;                  // key split of the item
   const HeadDesc& hd = a.heads[slot];
   const int qt = a.use_sel ? a.qt_sel[sel] : (BITS || !hd.qt_order) ? sel : ld_const(hd.qt_order + sel);
   const Geo g = a.g;
@@ -267,11 +271,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // each masked exactly on its own; the last entry's second half is dropped
   // when it lies wholly past the last token.
   const int sub = BITS ? 0 : a.sub;
-  const int e0 = BITS ? 0 : ld_const(hd.row_ptr + qt);
+  int e0 = BITS ? 0 : ld_const(hd.row_ptr + qt);
+  int len = BITS ? 0 : ld_const(hd.row_ptr + qt + 1) - e0;
+  if (!BITS && a.n_split > 1) {
+    // Entries of this split: the row's columns are ascending, so two binary
+    // searches find those in [c0, c1), the split's 128-key units in map
+    // k-tiles.
+    const int units = (N + 127) >> 7, per = 128 / (BK << sub);
+    const int c0 = (split * units / a.n_split) * per, c1 = ((split + 1) * units / a.n_split) * per;
+    auto lower = [&](int v) __attribute__((always_inline)) -> int {
+      int lo = 0, hi = len;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ld_const(hd.col + e0 + mid) < v) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
+    const int lo = lower(c0), hi = lower(c1);
+    e0 += lo;
+    len = hi - lo;
+  }
   const int32_t* __restrict__ col = hd.col + e0;
   const int n = [&]() __attribute__((always_inline)) -> int {
     if constexpr (BITS) return a.n_kt;
-    const int len = ld_const(hd.row_ptr + qt + 1) - e0;
     const int nn = len << sub;
     return (sub && len > 0 && ld_const(col + len - 1) * (BK << sub) + BK >= N) ? nn - 1 : nn;
   }();
@@ -846,6 +869,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int qp = q0 + gq * 32 + l32;
     const float l = sum_xor32(l_run[gq]);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
+    if (!BITS && !GTH && a.partial) {
+      // split partial (selected whole q-tiles only, so qp < N): fp32 rows
+      const int pr = (sel * a.n_split + split) * C::BQ + (qp - qt * C::BQ);
+      float* __restrict__ Op = (float*)hd.o + (size_t)pr * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          floatx4 ov;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ov[j] = acc[gq][db][i4 * 4 + j] * inv;
+          *(floatx4*)(Op + db * 32 + 8 * i4 + 4 * hh) = ov;
+        }
+      }
+      if (hh == 0) hd.lse[pr] = l > 0.f ? m_run[gq] * hd.scale + __logf(l) : -INFINITY;
+      continue;
+    }
     if (qp < N) {
       // gathered head: scatter to the row of position qp; compact output: rank-major rows
       const int qi = (GTH && hd.perm) ? hd.perm[qp] : a.compact ? sel * C::BQ + (qp - qt * C::BQ) : qp;

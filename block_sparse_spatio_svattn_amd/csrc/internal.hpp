@@ -180,6 +180,13 @@ struct FwdArgs {
   int32_t n_sel;          // work items per head: n_qt, or the number of selected q-tiles
   int32_t use_sel;        // 1: compute only q-tiles qt_sel[0 .. n_sel), the same for every head
   int32_t compact;        // 1: O / lse rows of selected q-tile i at i * block_q + row (with use_sel)
+  // Key splits per (head, q-tile) work item (1: whole rows; more only with use_sel and partial): split s
+  // takes the map entries whose keys lie in 128-key units [s U / n_split, (s + 1) U / n_split), U =
+  // ceil(N / 128), so a split covers the same keys whatever the map's block_k.
+  int32_t n_split;
+  // 1: O is fp32, normalised over the split's keys alone, with lse of the split (-inf when it keeps no
+  // key); rows of (selected q-tile i, split s) at (i * n_split + s) * block_q + row
+  int32_t partial;
   int32_t qt_sel[kMaxSelectedTiles];
   int32_t sub;            // map entries hold 1 << sub compute tiles (a 128-key map on the 64-key kernel: 1)
   int32_t dense_bits;     // 1: visit every k-tile and mask from bits
@@ -189,7 +196,12 @@ struct FwdArgs {
 
 hipError_t launch_forward(const FwdArgs& a, int head_dim, int block_q, int block_k, hipStream_t st);
 static_assert(sizeof(FwdArgs) <= 4096, "forward arguments must fit the kernel argument segment");
-hipError_t launch_route(const void* o_dense, const void* o_spatial, const void* o_temporal, int heads,
-                        int64_t per_head, int64_t valid, float* err, int32_t* choice, hipStream_t st);
+// Head routing from split partial outputs: o[m], lse[m] (m = dense, spatial, temporal) are
+// [heads][n_sel][n_split][block_q] rows of head_dim fp32 / one fp32, as the partial forward writes
+// them; perr holds heads * n_sel * block_q / route_rows_per_block(head_dim) pairs of fp32.
+constexpr int kRouteMergeThreads = 256, kRouteColsPerThread = 4;  // merge workgroup: 4 columns per thread
+inline int route_rows_per_block(int head_dim) { return kRouteMergeThreads / (head_dim / kRouteColsPerThread); }
+hipError_t launch_route(const float* const o[3], const float* const lse[3], int heads, int n_sel, int n_split,
+                        int block_q, int head_dim, float* perr, float* err, int32_t* choice, hipStream_t st);
 
 }  // namespace svattn

@@ -22,10 +22,14 @@ namespace {
 int g_fwd_launches = 0, g_map_launches = 0, g_perm_launches = 0, g_route_launches = 0;
 
 void check_fwd(const FwdArgs& a, int block_q, int block_k) {
-  if (a.n_slots < 1 || a.n_slots > kMaxHeadsPerLaunch || a.n_items != a.n_slots * a.n_sel) {
-    fprintf(stderr, "bad launch table: slots %d items %d sel %d\n", a.n_slots, a.n_items, a.n_sel);
+  if (a.n_slots < 1 || a.n_slots > kMaxHeadsPerLaunch || a.n_split < 1 || a.n_split > 32 ||
+      a.n_items != a.n_slots * a.n_sel * a.n_split) {
+    fprintf(stderr, "bad launch table: slots %d items %d sel %d splits %d\n", a.n_slots, a.n_items, a.n_sel,
+            a.n_split);
     abort();
   }
+  // key splits and partial outputs only for selected whole q-tiles
+  if ((a.n_split > 1 || a.partial) && (!a.use_sel || !a.compact || !a.partial)) abort();
   if (block_q < 32 || block_k < 32 || a.n_qt < 1 || a.n_kt < 1) abort();
   for (int i = 0; i < a.n_slots; ++i)
     if (!a.heads[i].q || !a.heads[i].k || !a.heads[i].v || !a.heads[i].o) abort();
@@ -65,9 +69,13 @@ hipError_t launch_permute(const Geo& g, int, int heads, int head_dim, const void
   ++g_perm_launches;
   return hipSuccess;
 }
-hipError_t launch_route(const void*, const void*, const void*, int heads, int64_t, int64_t, float*, int32_t*,
-                        hipStream_t) {
-  if (heads < 1) abort();
+hipError_t launch_route(const float* const o[3], const float* const lse[3], int heads, int n_sel, int n_split,
+                        int block_q, int head_dim, float* perr, float* err, int32_t* choice, hipStream_t) {
+  if (heads < 1 || n_sel < 1 || n_split < 1 || block_q % route_rows_per_block(head_dim) || !perr || !err ||
+      !choice)
+    abort();
+  for (int m = 0; m < 3; ++m)
+    if (!o[m] || !lse[m]) abort();
   ++g_route_launches;
   return hipSuccess;
 }
@@ -193,9 +201,10 @@ int main() {
     const svattn_mask tpf{SVATTN_TEMPORAL, SVATTN_FRAME_MAJOR, 0, 2};
     const int32_t qts[2] = {1, 5};
     expect(svattn_route_scratch_bytes(2, 128, 256, 2, &rb), SVATTN_OK, "route scratch: valid");
+    // routing keeps its work counter in the scratch and clears it itself: no device, so a HIP error
     expect(svattn_route_heads(&g, 2, 128, &spf, &tpf, &m, &m, &m, scales.data(), qts, 2, fake(0), fake(1), fake(2),
                               fake(6), rb, (float*)fake(7), (int32_t*)fake(8), nullptr),
-           SVATTN_OK, "route: valid");
+           SVATTN_ERR_HIP, "route: valid, no device");
     // with a workspace the ABI layer clears the work counter itself: no device, so a HIP error
     expect(svattn_forward(&g, 2, 128, masks.data(), maps.data(), scales.data(), fake(0), fake(1), fake(2), fake(3),
                           nullptr, fake(11), nullptr),

@@ -304,7 +304,10 @@ def test_route_validation():
     heads, d = 2, 64
     b = ctypes.c_size_t()
     assert L.svattn_route_scratch_bytes(heads, d, 64, 2, ctypes.byref(b)) == 0
-    assert b.value == 3 * heads * 2 * 64 * d * 2
+    # work counter, then per mask 32 key splits (1024 work items over 3 masks x 2 heads x 2 q-tiles, at
+    # most 32) of fp32 rows and their lse, then one pair of sums per 16-row merge workgroup
+    rows = heads * 2 * 32 * 64
+    assert b.value == 256 + 3 * (rows * d * 4 + rows * 4) + heads * 2 * (64 // 16) * 8
     assert L.svattn_route_scratch_bytes(heads, d, 64, 33, ctypes.byref(b)) == INVALID
     assert L.svattn_route_scratch_bytes(heads, 96, 64, 2, ctypes.byref(b)) == UNSUPPORTED
     sp, tp = sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.TEMPORAL, 0, 0, 1)

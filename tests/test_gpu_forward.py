@@ -584,3 +584,50 @@ def test_route_heads_against_oracle(sv, window, radius, bq):
         assert abs(err[h, 1] - et) <= 0.05 * et + 1e-7, (h, err[h], es, et)
         if abs(es - et) > 0.1 * max(es, et):
             assert ch[h] == (sv.TEMPORAL if choice == "temporal" else sv.SPATIAL), (h, es, et)
+
+
+@pytest.mark.parametrize("wl_name,bq,bk,qtiles", [("small", 64, 64, [0, 37, 74]), ("small", 256, 128, [3, 17]),
+                                                  ("small", 128, 32, list(range(0, 36, 2))),
+                                                  ("tiny", 32, 32, [0, 3, 7]), ("tiny", 64, 64, [1])])
+def test_route_heads_equals_plain_forward(sv, wl_name, bq, bk, qtiles):
+    """Routing runs its forward with the key list cut into splits merged by
+    their lse; its deviations equal those of the plain forward's bf16 outputs
+    over the same rows to 1% (a merged element may round to the neighbouring
+    bf16 value), and its choice agrees wherever those differ by more than 2%.
+    Covers head_dim 64 and 128, 32- to 128-key maps, 1 to 18 q-tiles (up to
+    32 splits, many of them without a kept key on the small grids)."""
+    wl = synth.WORKLOADS[wl_name]
+    inp = synth.make_inputs(wl)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    g, sp, tp, dm, sm, tm = _route_setup(sv, wl, 1, 2, bq=bq, bk=bk)
+    err, ch = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, qtiles)
+    H = wl.n_heads
+    outs = [sv.forward(g, q, k, v, [m] * H, [mp] * H, scales)
+            for m, mp in ((sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0), dm), (sp, sm), (tp, tm))]
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(t * bq, (t + 1) * bq) for t in qtiles])
+    od, osp, ot = (f64_of(o)[:, rows] for o in outs)
+    es = ((osp - od) ** 2).mean(axis=(1, 2))
+    et = ((ot - od) ** 2).mean(axis=(1, 2))
+    err, ch = err.cpu().numpy().astype(np.float64), ch.cpu().numpy()
+    for h in range(H):
+        assert abs(err[h, 0] - es[h]) <= 0.01 * es[h] + 1e-9, (h, err[h], es[h])
+        assert abs(err[h, 1] - et[h]) <= 0.01 * et[h] + 1e-9, (h, err[h], et[h])
+        if abs(es[h] - et[h]) > 0.02 * max(es[h], et[h]):
+            assert ch[h] == (sv.TEMPORAL if et[h] < es[h] else sv.SPATIAL), (h, es[h], et[h])
+
+
+def test_route_heads_repeat_is_deterministic(sv):
+    """The split forward takes its work from a shared counter, but each split
+    writes its own rows and the merge sums in a fixed order: two calls give
+    bit-identical deviations."""
+    wl = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(wl)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    g, sp, tp, dm, sm, tm = _route_setup(sv, wl, 1, 2, bq=64, bk=64)
+    a, _ = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, [5, 50])
+    b, _ = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, [5, 50])
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))

@@ -147,3 +147,42 @@ def test_p1440_every_qtile(sv, heads):
     """302,400 tokens x 10 heads: one row per q-tile (1,182 per head) plus the
     last row, split over five tests to bound each one's oracle time."""
     _run_case(sv, "p1440", "tmb", heads, per_tile=1, check_lse=True)
+
+
+def test_headline_routing_against_oracle(sv):
+    """Head routing at full size in the benchmark's configuration: 75,600
+    tokens, 10 heads, the two q-tiles the benchmark samples (rows of the
+    frame-major order), 256 x 64 maps, the split forward (18 key splits per
+    q-tile).  Every head's two deviations within 2% of the oracle's (fp64
+    outputs of the same 512 rows), and the choice agrees wherever the
+    oracle's two deviations differ by more than 5%."""
+    wl = synth.WORKLOADS["headline"]
+    inp = _inputs("headline")
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    og = oracle.Geometry(wl.frames, wl.height, wl.width)
+    window = next(h.window for h in wl.heads if h.kind == synth.SPATIAL)
+    radius = next(h.radius for h in wl.heads if h.kind == synth.TEMPORAL)
+    sp = sv.Mask(sv.SPATIAL, sv.FRAME_MAJOR, window, 0)
+    tp = sv.Mask(sv.TEMPORAL, sv.FRAME_MAJOR, 0, radius)
+    maps = [sv.build_tile_map(g, m, BQ, BK) for m in (sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0), sp, tp)]
+    n_full = wl.n_tokens // BQ
+    qtiles = [n_full // 3, (2 * n_full) // 3]
+    print(f"routing headline q-tiles {qtiles}", flush=True)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    err, ch = sv.route_heads(g, q, k, v, sp, tp, *maps, scales, qtiles)
+    torch.cuda.synchronize()
+    err, ch = err.cpu().numpy(), ch.cpu().numpy()
+    rows = np.concatenate([np.arange(t * BQ, (t + 1) * BQ) for t in qtiles])
+
+    def oracle_head(h):
+        return oracle.route_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), og, window, radius, rows)
+
+    with ThreadPoolExecutor(4) as ex:
+        refs = list(ex.map(oracle_head, range(wl.n_heads)))
+    for h, (es, et, choice) in enumerate(refs):
+        print(json.dumps({"head": h, "err": [float(err[h, 0]), float(err[h, 1])], "oracle": [es, et]}), flush=True)
+        assert abs(err[h, 0] - es) <= 0.02 * es + 1e-9, (h, err[h], es, et)
+        assert abs(err[h, 1] - et) <= 0.02 * et + 1e-9, (h, err[h], es, et)
+        if abs(es - et) > 0.05 * max(es, et):
+            assert ch[h] == (sv.TEMPORAL if choice == "temporal" else sv.SPATIAL), (h, es, et)
