@@ -294,7 +294,10 @@ SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int3
  * neither the rows nor the deviation; here the rows are the selected whole
  * q-tiles of the frame-major order (block_q rows each) and the deviation is
  * the mean squared difference of the bf16 outputs over those rows and all
- * head_dim columns; a tie goes to the spatial mask.
+ * head_dim columns; a tie goes to the spatial mask.  Each output row is
+ * computed as several key splits merged by their log-sum-exp (the same
+ * softmax up to fp32 rounding), then rounded to bf16.  Results are
+ * deterministic.
  *   spatial, temporal  the two candidate masks, FRAME_MAJOR (window / radius
  *          as for svattn_forward; the same for every head)
  *   dense_map, spatial_map, temporal_map  tile maps of the frame-major order
@@ -305,7 +308,12 @@ SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int3
  *          wholly inside the sequence ((qtile + 1) * block_q <= N)
  *   q, k, v frame-major [heads, N, head_dim] bf16 (16-byte aligned)
  *   scratch device memory of svattn_route_scratch_bytes() bytes (16-byte
- *          aligned), caller-owned; holds the three outputs of the sampled rows
+ *          aligned), caller-owned, needs no clearing; holds a work counter,
+ *          the three outputs of the sampled rows as key splits (fp32 rows
+ *          normalised over each split's keys, with their lse; the split
+ *          count depends on heads and n_qtiles only) and the per-workgroup
+ *          sums of the merge.  Two calls sharing a scratch must not overlap
+ *          in time.
  *   err    device fp32 [heads, 2]: deviation of the spatial and the temporal
  *          output;  choice  device int32 [heads]: SVATTN_SPATIAL or
  *          SVATTN_TEMPORAL
