@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
     L.svattn_forward_ptrs.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
                                       P(_vp), P(_vp), P(_vp), P(_vp), P(_vp), _vp, _vp]
     L.svattn_forward_fused.argtypes = [P(Geom), _i32, _i32, P(Mask), P(P(_TileMapC)), P(ctypes.c_float),
-                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.svattn_route_scratch_bytes.argtypes = [_i32, _i32, _i32, _i32, P(ctypes.c_size_t)]
     L.svattn_route_heads.argtypes = [P(Geom), _i32, _i32, P(Mask), P(Mask), P(_TileMapC), P(_TileMapC),
                                      P(_TileMapC), P(ctypes.c_float), P(_i32), _i32, _vp, _vp, _vp, _vp,
@@ -292,12 +292,12 @@ def forward(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 def forward_fused(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   masks: Sequence[Mask], maps: Sequence[TileMap], scales: Sequence[float],
-                  perm: Optional[torch.Tensor], out: Optional[torch.Tensor] = None,
-                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Forward over frame-major [heads, N, d] tensors with the temporal-major
-    permutation fused in: heads whose mask order is TEMPORAL_MAJOR are computed
-    in that order through ``perm`` (int32 [N] from permutation_index)."""
+    permutation fused in: a head whose mask order is temporal-major is
+    computed in that order, the kernel reading and writing the rows of its
+    positions in place (no permuted copies)."""
     heads = q.shape[0]
     out = _qkvo(q, k, v, out, geom.n)
     if len(masks) != heads or len(maps) != heads:
@@ -306,9 +306,8 @@ def forward_fused(geom: Geom, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     P = ctypes.POINTER(_TileMapC)
     parr = (P * heads)(*[ctypes.pointer(m.c) for m in maps])
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
-    perm_p = _dev(perm, "perm", torch.int32) if perm is not None else None
     _check(lib().svattn_forward_fused(ctypes.byref(geom), heads, q.shape[2], marr, parr, _scales(scales, heads),
-                                      perm_p, _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                                      _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
                                       _dev(v, "v", torch.bfloat16), _dev(out, "o", torch.bfloat16),
                                       lse_p, _ws(workspace), _stream(stream)), "svattn_forward_fused")
     return out

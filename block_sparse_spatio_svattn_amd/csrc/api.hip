@@ -150,7 +150,7 @@ hipError_t dispatch_forward(const FwdArgs& a, int head_dim, int bq, int bk, hipS
     return head_dim == 128 ? launch_forward_d128_bits(a, bq, bk, st) : launch_forward_d64_bits(a, bq, bk, st);
   bool all_dense = true;
   for (int i = 0; i < a.n_slots; ++i)
-    all_dense = all_dense && a.heads[i].kind == SVATTN_DENSE && !a.heads[i].perm;  // gathered: plain schedule
+    all_dense = all_dense && a.heads[i].kind == SVATTN_DENSE && !a.heads[i].gather;  // gathered: plain schedule
   return head_dim == 128 ? launch_forward_d128_map(a, bq, bk, all_dense, st)
                          : launch_forward_d64_map(a, bq, bk, all_dense, st);
 }
@@ -392,7 +392,7 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
 static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32_t head_dim,
                         const svattn_mask* masks, const svattn_tile_map* const* maps, const float* scales,
                         const std::vector<HeadPtrs>& ptrs, void* workspace, void* stream,
-                        const int32_t* perm = nullptr, bool use_scratch = false) {
+                        bool gather = false, bool use_scratch = false) {
   int s;
   if (!masks || !maps) return fail(SVATTN_ERR_INVALID_ARG, "masks / maps is NULL");
   int bq = 0, bk = 0;
@@ -438,7 +438,7 @@ static int forward_impl(const svattn_geom* geom, int64_t n, int32_t heads, int32
     d.col = maps[h]->col;
     d.col_cls = maps[h]->col_cls;
     d.qt_order = maps[h]->qt_order;
-    d.perm = masks[h].order != SVATTN_FRAME_MAJOR ? perm : nullptr;
+    d.gather = gather && masks[h].order != SVATTN_FRAME_MAJOR;
     d.scale = scales[h];
     d.scale_log2 = scales[h] * kLog2eHost;
     d.kind = masks[h].kind;
@@ -491,7 +491,7 @@ int svattn_forward_noalloc(const svattn_geom* geom, int32_t heads, int32_t head_
   if ((s = check_common(heads, head_dim, scales))) return s;
   if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
   return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
-                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), nullptr, stream, nullptr, true);
+                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), nullptr, stream, false, true);
 }
 
 int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
@@ -509,32 +509,15 @@ int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32_t head_dim
 }
 
 int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_dim, const svattn_mask* masks,
-                         const svattn_tile_map* const* maps, const float* scales, const int32_t* perm, const void* q,
-                         const void* k, const void* v, void* o, float* lse, void* workspace, void* stream) {
+                         const svattn_tile_map* const* maps, const float* scales, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* workspace, void* stream) {
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
   if ((s = check_common(heads, head_dim, scales))) return s;
   if (!q || !k || !v || !o) return fail(SVATTN_ERR_INVALID_ARG, "q / k / v / o is NULL");
-  if (!masks) return fail(SVATTN_ERR_INVALID_ARG, "masks is NULL");
-  bool any_tm = false, any_tmb = false;
-  for (int h = 0; h < heads; ++h) {
-    any_tm = any_tm || masks[h].order == SVATTN_TEMPORAL_MAJOR;
-    any_tmb = any_tmb || masks[h].order == SVATTN_TEMPORAL_MAJOR_BLOCKED;
-  }
-  if (any_tm && any_tmb)
-    return fail(SVATTN_ERR_INVALID_ARG, "one perm serves one temporal-major order: the call mixes both");
-  any_tm = any_tm || any_tmb;
-  if (any_tm) {
-    if (!perm) return fail(SVATTN_ERR_INVALID_ARG, "perm is NULL but a head runs in temporal-major order");
-    if (!aligned(perm, 4)) return fail(SVATTN_ERR_INVALID_ARG, "perm must be 4-byte aligned");
-    const size_t pb = (size_t)n * 4, ob = (size_t)heads * n * head_dim * 2;
-    if (overlap(perm, pb, o, ob) || (lse && overlap(perm, pb, lse, (size_t)heads * n * 4)) ||
-        (workspace && overlap(perm, pb, workspace, SVATTN_FORWARD_WORKSPACE_BYTES)))
-      return fail(SVATTN_ERR_INVALID_ARG, "perm overlaps an output or the workspace");
-  }
   return forward_impl(geom, n, heads, head_dim, masks, maps, scales,
-                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream, any_tm ? perm : nullptr);
+                      contiguous_ptrs(n, heads, head_dim, q, k, v, o, lse), workspace, stream, true);
 }
 
 // Key splits per (head, q-tile) of a routing launch: enough work items (three

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   static_assert(!GTH || (!PP && !BITS), "gathered heads run the plain schedule over tile maps");
   // Tiles per barrier of the plain schedule: the d128, 256 x 64 launch runs
   // two tiles between barriers (four LDS stages, 132 KB), the others one.
-  constexpr int TPB = (!PP && !GTH && !BITS && D == 128 && BK == 64 && NW == 8) ? 2 : 1;
+  constexpr int TPB = (!PP && !BITS && D == 128 && BK == 64 && NW == 8) ? 2 : 1;
   constexpr int STAGES = PP ? 3 : 2 * TPB;
   __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
     const int qi = min(q0 + gq * 32 + l32, N - 1);
-    const int qr = (GTH && hd.perm) ? hd.perm[qi] : qi;  // gathered head: the row holding position qi
+    const int qr = (GTH && hd.gather) ? tm_to_fm(g, order, qi) : qi;  // gathered head: the row of position qi
 #pragma unroll
     for (int ds = 0; ds < C::DS; ++ds) qf[gq][ds] = *(const bf16x8*)(Q + (size_t)qr * D + ds * 16 + hh * 8);
   }
@@ -364,20 +364,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bool real = row < BK && slot < C::CPR;
     dma_off[i] = real ? (row * D + (is_k ? slot : (slot ^ vswz<D>(row))) * 8) * 2 : 0;
   }
-  // Gathered heads (hd.perm set): the tensor row holding each lane's key of
-  // every piece, loaded ahead of the copies (a load on the copy's critical
-  // path would stall it).
-  int prow[GTH ? OPC : 1];
-  const bool gathered = GTH && hd.perm != nullptr;
-  auto gather_rows = [&](int key0) __attribute__((always_inline)) {
-    if constexpr (GTH) {
-#pragma unroll
-      for (int i = 0; i < OPC; ++i) prow[i] = hd.perm[min(key0 + dma_off[i] / (D * 2), N - 1)];
-    }
+  // Gathered heads: the tensors are frame-major and the head runs in a
+  // temporal-major order; the row holding position t' is a closed form of
+  // the geometry (tm_to_fm), so a gathered copy waits on no load.  Lane j of
+  // a wave works out the row of the tile's key j once per tile, and each copy
+  // takes the row of its key from that lane (a cross-lane read): one closed
+  // form per lane and tile instead of one per copy.
+  static_assert(BK <= 64, "one lane per key of a tile");
+  const bool gathered = GTH && hd.gather;
+  auto tile_rows = [&](int key0) __attribute__((always_inline)) -> int {
+    if constexpr (GTH) return gathered ? tm_to_fm(g, order, min(key0 + lane, N - 1)) : 0;
+    return 0;
   };
   // Copy i of this wave for the tile starting at key0, into stage st (ragged:
   // the tile runs past the last token).
-  auto issue_op = [&](int i, int key0, int st, bool ragged) __attribute__((always_inline)) {
+  auto issue_op = [&](int i, int key0, int st, bool ragged, int rows) __attribute__((always_inline)) {
     const bool is_k = i < KOPS;
     const int pc = op_piece(i);
     if (cw < 0) return;
@@ -391,8 +392,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b64 >> 32)) << 32) |
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
     uint32_t off = (uint32_t)dma_off[i];
-    if (gathered) {  // row prow[i] of the tensor, same chunk
-      if constexpr (GTH) off = (uint32_t)prow[i] * (uint32_t)(D * 2) + (uint32_t)(dma_off[i] % (D * 2));
+    if (gathered) {  // the row holding the key's position (the last one past N), same chunk
+      if constexpr (GTH) {
+        const int row = __builtin_amdgcn_ds_bpermute((int)(off / (D * 2)) << 2, rows);
+        off = (uint32_t)row * (uint32_t)(D * 2) + off % (D * 2);
+      }
     } else if (ragged) {  // rows past N read row N-1 (their keys are masked)
       const int row = (int)(off / (D * 2));
       off = (uint32_t)((min(key0 + row, N - 1) - key0) * (D * 2) + (off - row * (D * 2)));
@@ -408,12 +412,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   // All copies of a tile at once (one branch for a ragged tile).
   auto issue = [&](int key0, int st) __attribute__((always_inline)) {
+    const int rows = tile_rows(key0);
     if (key0 + BK > N) {
 #pragma unroll
-      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, true);
+      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, true, rows);
     } else {
 #pragma unroll
-      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, false);
+      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, false, rows);
     }
     issue_kc(key0, st);
   };
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (!dma) return;
 #pragma unroll
     for (int i = 0; i < OPC; ++i)
-      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st, key0 + BK > N);
+      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st, key0 + BK > N, 0);  // the two-group schedule never gathers
   };
   auto next_stage = [&](int st) __attribute__((always_inline)) { return st == STAGES - 1 ? 0 : st + 1; };
 
@@ -816,8 +821,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i <= TPB; ++i) fetch(i, wk[i], wc[i]);
     if (n > 0) {
-      if constexpr (GTH)
-        if (gathered) gather_rows(wk[0]);
       issue(wk[0], 0);
     }
     if constexpr (TPB == 2)
@@ -832,8 +835,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (u == 0 || t < n) {
           const int st = grp + u;
           fetch(t + TPB + 1, wk[TPB + 1], wc[TPB + 1]);
-          if constexpr (GTH)
-            if (gathered && t + 1 < n) gather_rows(wk[1]);
           // a wave whose queries keep no key of this tile skips S, softmax and P V
           uint64_t keep[QG];
           const int ms = plan(st, wk[0], wc[0], keep);
@@ -888,7 +889,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     if (qp < N) {
       // gathered head: scatter to the row of position qp; compact output: rank-major rows
-      const int qi = (GTH && hd.perm) ? hd.perm[qp] : a.compact ? sel * C::BQ + (qp - qt * C::BQ) : qp;
+      const int qi = (GTH && hd.gather) ? tm_to_fm(g, order, qp) : a.compact ? sel * C::BQ + (qp - qt * C::BQ) : qp;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -963,7 +964,7 @@ template <int D, int BK, int NW, int QG, bool PP, bool BITS = false>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
   if constexpr (!PP && !BITS) {
     bool gather = false;
-    for (int i = 0; i < a.n_slots; ++i) gather = gather || a.heads[i].perm != nullptr;
+    for (int i = 0; i < a.n_slots; ++i) gather = gather || a.heads[i].gather;
     if (gather) return launch_sched<D, BK, NW, QG, PP, BITS, true>(a, st);
   }
   return launch_sched<D, BK, NW, QG, PP, BITS, false>(a, st);

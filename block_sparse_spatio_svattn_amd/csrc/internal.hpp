@@ -154,7 +154,7 @@ struct HeadDesc {
   const int32_t* col;
   const uint8_t* col_cls;
   const int32_t* qt_order;  // visiting order of q-tiles, or nullptr for index order
-  const int32_t* perm;      // row of q/k/v/o holding layout position t' (gathered head), or nullptr
+  int32_t gather;           // 1: q/k/v/o are frame-major, position t' of `order` is row tm_to_fm(t')
   const uint32_t* bits;  // dense-mask mode: [N][ceil(N/32)] words of this head
   float scale_log2;      // scale * log2(e)
   float scale;

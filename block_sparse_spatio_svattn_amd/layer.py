@@ -15,7 +15,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import torch
 
 from . import (FRAME_MAJOR, Geom, Mask, SvattnError, TileMap, build_tile_map, new_workspace, forward_fused,
-               forward_ptrs, permutation_index, permute_tokens, unpermute)
+               forward_ptrs, permute_tokens, unpermute)
 
 
 def _runs(idx: List[int], key=lambda h: 0) -> List[Tuple[int, int]]:
@@ -52,15 +52,9 @@ class SparseVideoAttention:
         self._buf = None
         # work counter of the persistent schedule (None: static grid)
         self.workspace = new_workspace(device) if persistent else None
-        # fused: temporal-major heads read and write the frame-major tensors
-        # through the permutation index instead of permuted copies
+        # fused: temporal-major heads read and write the rows of their
+        # positions in the frame-major tensors instead of permuted copies
         self.fused = fused
-        self.perm = None
-        if fused and self.tm_heads:
-            orders = {self.masks[h].order for h in self.tm_heads}
-            if len(orders) > 1:
-                raise SvattnError("fused: all temporal-major heads must share one token order")
-            self.perm = permutation_index(geom, device=device, order=orders.pop())[0]
 
     def _buffers(self):
         if self._buf is None:
@@ -111,7 +105,7 @@ class SparseVideoAttention:
             raise SvattnError(f"expected q/k/v of shape {(H, self.geom.n, self.head_dim)}")
         out = torch.empty_like(q) if out is None else out
         if self.fused:
-            forward_fused(self.geom, q, k, v, self.masks, self.maps, scales, self.perm, out=out,
+            forward_fused(self.geom, q, k, v, self.masks, self.maps, scales, out=out,
                           workspace=self.workspace, stream=stream)
             return out
         self.permute_inputs(q, k, v, stream)

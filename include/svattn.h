@@ -264,27 +264,23 @@ SVATTN_API int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32
                                    void* workspace, void* stream);
 
 /*
- * Forward with the temporal-major permutation fused in: Q, K, V, O (and lse)
- * of every head stay in frame-major order ([heads, N, head_dim] as for
- * svattn_forward), and heads whose mask has a temporal-major order
- * (TEMPORAL_MAJOR or TEMPORAL_MAJOR_BLOCKED, maps built for that order; all
- * such heads of a call share one of the two) are computed in that order by
- * reading the rows of their tensors through perm and writing their O and lse
- * rows back through it (ainews.tenesys.com, "Co się zmieniło?", item 5,
- * without the separate reordering passes).  The result equals
+ * Forward with the temporal-major permutation fused in (ainews.tenesys.com,
+ * "Co się zmieniło?", item 5, without the separate reordering passes): Q, K,
+ * V, O (and lse) of every head stay in frame-major order ([heads, N,
+ * head_dim] as for svattn_forward), and a head whose mask has a
+ * temporal-major order (TEMPORAL_MAJOR or TEMPORAL_MAJOR_BLOCKED, its map
+ * built for that order; heads may use either) is computed in that order: the
+ * kernel reads the row holding each position, which is a closed form of the
+ * geometry (the permutation svattn_permutation_index_order writes), and
+ * writes its O and lse rows back the same way.  The result equals
  * svattn_permute_tokens_order, then svattn_forward, then
- * svattn_unpermute_order, bit for bit.
- *   perm  device int32 [N]: perm[t'] = frame-major token at position t' of
- *         that order (svattn_permutation_index_order); 4-byte aligned; may be
- *         NULL if no head runs in a temporal-major order; must not overlap o,
- *         lse or the workspace.  SVATTN_ERR_INVALID_ARG if the call mixes the
- *         two temporal-major orders.
- * Other arguments as for svattn_forward.
+ * svattn_unpermute_order, bit for bit.  Arguments, errors and workspace as
+ * for svattn_forward.
  */
 SVATTN_API int svattn_forward_fused(const svattn_geom* geom, int32_t heads, int32_t head_dim,
                                     const svattn_mask* masks, const svattn_tile_map* const* maps,
-                                    const float* scales, const int32_t* perm, const void* q, const void* k,
-                                    const void* v, void* o, float* lse, void* workspace, void* stream);
+                                    const float* scales, const void* q, const void* k, const void* v, void* o,
+                                    float* lse, void* workspace, void* stream);
 
 /*
  * Head routing (aihirek.info, section "A Sparse VideoGen a figyelmi fejeket

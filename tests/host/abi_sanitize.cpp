@@ -31,8 +31,11 @@ void check_fwd(const FwdArgs& a, int block_q, int block_k) {
   // key splits and partial outputs only for selected whole q-tiles
   if ((a.n_split > 1 || a.partial) && (!a.use_sel || !a.compact || !a.partial)) abort();
   if (block_q < 32 || block_k < 32 || a.n_qt < 1 || a.n_kt < 1) abort();
-  for (int i = 0; i < a.n_slots; ++i)
-    if (!a.heads[i].q || !a.heads[i].k || !a.heads[i].v || !a.heads[i].o) abort();
+  for (int i = 0; i < a.n_slots; ++i) {
+    const HeadDesc& h = a.heads[i];
+    if (!h.q || !h.k || !h.v || !h.o) abort();
+    if (h.gather && h.order == SVATTN_FRAME_MAJOR) abort();  // only temporal-major heads gather
+  }
   ++g_fwd_launches;
 }
 }  // namespace
@@ -186,8 +189,8 @@ int main() {
     expect(svattn_forward_ptrs(&g, H, 128, masks.data(), maps.data(), scales.data(), qp.data(), kp.data(),
                                vp.data(), op.data(), lp.data(), nullptr, nullptr),
            SVATTN_OK, "forward_ptrs: valid");
-    expect(svattn_forward_fused(&g, H, 128, masks.data(), maps.data(), scales.data(), (const int32_t*)fake(5),
-                                fake(0), fake(1), fake(2), fake(3), nullptr, nullptr, nullptr),
+    expect(svattn_forward_fused(&g, H, 128, masks.data(), maps.data(), scales.data(), fake(0), fake(1), fake(2),
+                                fake(3), nullptr, nullptr, nullptr),
            SVATTN_OK, "forward_fused: valid");
     svattn_tile_map m128 = map_of(g, 256, 128);
     std::vector<const svattn_tile_map*> maps128(H, &m128);

@@ -270,6 +270,9 @@ def test_traffic_summary_parses():
 
 
 def test_forward_fused_validation():
+    """The fused entry takes svattn_forward's arguments and checks them the
+    same way; heads may mix the two temporal-major orders (each head's rows
+    follow from its own order)."""
     L = sv.lib()
     g = sv.Geom(4, 8, 8)   # N = 256
     heads, d = 2, 64
@@ -279,23 +282,18 @@ def test_forward_fused_validation():
     parr = (P * heads)(ctypes.pointer(m), ctypes.pointer(m))
     sarr = (ctypes.c_float * heads)(0.1, 0.1)
     q, k, v, o = FAKE, FAKE * 16, FAKE * 32, FAKE * 64
-    f = lambda perm, **kw: L.svattn_forward_fused(ctypes.byref(g), heads, d, marr, parr, sarr, perm, q, k, v,
-                                                  kw.get("o", o), None, kw.get("ws"), None)
-    assert f(None) == INVALID                     # a temporal-major head needs perm
-    assert "perm" in _err()
-    assert f(FAKE * 128 + 2) == INVALID           # misaligned
-    assert f(FAKE * 64 + 1024) == INVALID         # perm inside o
-    assert f(FAKE * 128, ws=FAKE * 128) == INVALID  # perm overlaps the workspace
-    # one perm cannot serve both temporal-major orders
+    f = lambda masks=marr, **kw: L.svattn_forward_fused(ctypes.byref(g), heads, d, masks, parr, sarr,
+                                                        kw.get("q", q), k, v, kw.get("o", o), None, kw.get("ws"),
+                                                        None)
+    assert f(o=FAKE * 16 + 1024) == INVALID        # o inside k
+    assert f(q=FAKE + 8) == INVALID                # misaligned q
+    assert f(ws=FAKE * 64 + 256) == INVALID        # workspace inside o
+    bad = (sv.Mask * heads)(sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 1), sv.Mask(7, 0, 1, 0))
+    assert f(masks=bad) == INVALID                 # unknown mask kind
+    # both temporal-major orders in one call pass validation (fails later only for lack of a device)
     mixed = (sv.Mask * heads)(sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 1),
                               sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR_BLOCKED, 0, 1))
-    assert L.svattn_forward_fused(ctypes.byref(g), heads, d, mixed, parr, sarr, FAKE * 128, q, k, v, o, None, None,
-                                  None) == INVALID
-    assert "mixes" in _err()
-    # frame-major heads only: perm may be NULL (fails later only for lack of a device)
-    fm = (sv.Mask * heads)(sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.DENSE, 0, 0, 0))
-    got = L.svattn_forward_fused(ctypes.byref(g), heads, d, fm, parr, sarr, None, q, k, v, o, None, None, None)
-    assert got != INVALID or "perm" not in _err()
+    assert f(masks=mixed) != INVALID
 
 
 def test_route_validation():

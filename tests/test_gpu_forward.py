@@ -434,8 +434,8 @@ def test_tile_aligned_long_runs(sv):
                                                       ("small", 256, 64, True), ("small", 128, 32, False)])
 def test_fused_permutation_bit_identical(sv, wl_name, bq, bk, persistent):
     """Temporal-major heads computed straight from the frame-major tensors
-    (rows gathered through the permutation index, O scattered back) give the
-    same bits as permute -> forward -> unpermute."""
+    (the row of each position worked out in the kernel, O scattered back)
+    give the same bits as permute -> forward -> unpermute."""
     from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
     wl = synth.WORKLOADS[wl_name]
     inp = synth.make_inputs(wl)
@@ -449,13 +449,16 @@ def test_fused_permutation_bit_identical(sv, wl_name, bq, bk, persistent):
     assert (bits_of(o_sep) == bits_of(o_fused)).all()
 
 
-@pytest.mark.parametrize("geom,bq,bk", [((4, 8, 8), 256, 64), ((5, 24, 40), 128, 64), ((17, 9, 13), 64, 32)])
-def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk):
-    """Fused and separate paths agree bit for bit with the temporal heads in the
-    blocked order; both within the bar of the oracle."""
+@pytest.mark.parametrize("geom,bq,bk,second", [((4, 8, 8), 256, 64, "tmb"), ((5, 24, 40), 128, 64, "tmb"),
+                                               ((17, 9, 13), 64, 32, "tmb"), ((5, 24, 40), 256, 64, "tm"),
+                                               ((21, 9, 14), 256, 64, "tm")])
+def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk, second):
+    """Fused and separate paths agree bit for bit with temporal heads in the
+    blocked order (and, second = "tm", a head of the raster temporal-major
+    order in the same call); both within the bar of the oracle."""
     from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
     heads = (synth.Head("spatial", window=1), synth.Head("temporal", radius=2, order="tmb"),
-             synth.Head("temporal", radius=1, order="tmb"))
+             synth.Head("temporal", radius=1, order=second))
     F, H, W = geom
     wl = synth.Workload(name="fb", seed=37, frames=F, height=H, width=W, head_dim=128, heads=heads,
                         tiles=((bq, bk),))
@@ -470,7 +473,7 @@ def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk):
     assert (bits_of(o_sep) == bits_of(o_fused)).all()
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * len(heads))
     for h in range(len(heads)):
-        assert_close(f64_of(o_fused[h]), ref[h][0], f"fused tmb {geom} h{h}")
+        assert_close(f64_of(o_fused[h]), ref[h][0], f"fused tmb/{second} {geom} h{h}")
 
 
 def test_fused_permutation_lse_and_ragged_long_runs(sv):
@@ -490,7 +493,7 @@ def test_fused_permutation_lse_and_ragged_long_runs(sv):
     ws = sv.new_workspace()
     n = wl.n_tokens
     lse_f = torch.empty(len(heads), n, dtype=torch.float32, device="cuda")
-    o_f = sv.forward_fused(g, q, k, v, masks, maps, scales, perm, lse=lse_f, workspace=ws)
+    o_f = sv.forward_fused(g, q, k, v, masks, maps, scales, lse=lse_f, workspace=ws)
     # separate path: permuted copies of every temporal-major head
     tm = [h for h, m in enumerate(masks) if m.order == sv.TEMPORAL_MAJOR]
     qs, ks, vs = q.clone(), k.clone(), v.clone()
