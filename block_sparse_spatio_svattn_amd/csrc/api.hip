@@ -114,7 +114,7 @@ int check_map_buffers(const svattn_tile_map* map, const char* who) {
 // Clears the work counter of the persistent schedule.  A kernel rather than a
 // memset, so that a captured graph replays it correctly.
 __global__ void clear_queue_kernel(uint32_t* q) {
-  if (threadIdx.x == 0) q[0] = 0u;
+  if (threadIdx.x < 8) q[threadIdx.x] = 0u;  // the eight per-XCD work counters
 }
 
 // Work counter area of svattn_forward_noalloc, for callers that cannot

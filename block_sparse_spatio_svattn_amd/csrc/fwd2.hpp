@@ -95,6 +95,7 @@ constexpr int VPF = SVATTN_VPF;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr uint32_t kXcdBlock = 32;          // consecutive work items dealt to one XCD
 constexpr float kSumBound = 256.0f;         // 2^kRescaleThreshold
 constexpr float kNegBig = -1.0e30f;        // initial running max (finite)
 
@@ -161,6 +162,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   __shared__ int ticket;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // Persistent schedule: one work counter per XCD (workgroup b runs on XCD
+  // b % 8).  Counter x deals items in blocks of kXcdBlock consecutive items,
+  // block j of XCD x being items [(8 j + x) kXcdBlock, ...), so each XCD's
+  // L2 serves neighbouring items of the longest-first order, and every XCD
+  // starts on the longest ones.  An XCD whose counter runs dry takes items
+  // from the next XCD's counter (thread 0's state; at most eight counters
+  // are found dry, so every workgroup ends).
+  int xq = blockIdx.x & 7, xdry = 0;
+  auto next_item = [&]() __attribute__((always_inline)) -> int {
+    while (xdry < 8) {
+      const uint32_t t = atomicAdd(a.queue + xq, 1u);
+      const int it = (int)(((t / kXcdBlock) * 8u + (uint32_t)xq) * kXcdBlock + t % kXcdBlock);
+      if (it < a.n_items) return it;
+      xq = (xq + 1) & 7;
+      ++xdry;
+    }
+    return a.n_items;
+  };
 
   // ---- work items ----
   // Static schedule (no queue): one item per workgroup, XCD-aware (workgroup
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int xcd = b & 7, s = b >> 3;
     item = ((s / a.chunk) * 8 + xcd) * a.chunk + (s % a.chunk);
   } else {
-    if (tid == 0) ticket = (int)atomicAdd(a.queue, 1u);
+    if (tid == 0) ticket = next_item();
     __syncthreads();
     item = __builtin_amdgcn_readfirstlane(ticket);
   }
@@ -908,7 +927,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   if constexpr (!PST) break;
   __syncthreads();  // every wave has read the previous ticket
-  if (tid == 0) ticket = (int)atomicAdd(a.queue, 1u);
+  if (tid == 0) ticket = next_item();
   __syncthreads();
   item = __builtin_amdgcn_readfirstlane(ticket);
   }  // items
