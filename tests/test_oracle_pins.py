@@ -513,3 +513,52 @@ def test_route_head_closed_forms():
     vc = np.full_like(v, v[0, 0])
     es, et, _ = oracle.route_head(q, k, vc, 0.25, g, 0, 1, rows)
     assert es < 1e-28 and et < 1e-28
+
+
+def test_route_head_deviation_by_brute_force():
+    """With Q = 0 every kept key gets the same weight, so each output row is
+    the plain mean of V over the row's kept keys.  The deviations are then
+    recomputed here from the mask definitions alone (spatial: frames within w,
+    temporal: patches within Chebyshev distance r, both plus every frame-0
+    key), one Python loop per row and key, and must equal route_head's: this
+    pins the deviation measure (mean over rows and columns of the squared
+    difference) and both candidate masks, not only the zero cases."""
+    F, H, W, d = 3, 3, 4, 8
+    g = Geometry(F, H, W)
+    rng = np.random.Generator(np.random.PCG64(77))
+    n = F * H * W
+    q = np.zeros((n, d), dtype=np.uint16)  # bf16 bit patterns, as every oracle input
+    k = synth.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    vb = synth.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    v = (vb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # bf16 widened exactly
+    rows = np.array([0, 5, 13, 20, 29, 35])
+    w, r = 1, 1
+
+    def coords(t):
+        f, p = divmod(t, H * W)
+        return f, p // W, p % W
+
+    def kept(kind, a, b):
+        fa, ya, xa = coords(a)
+        fb, yb, xb = coords(b)
+        if fb == 0:
+            return True
+        if kind == "spatial":
+            return abs(fa - fb) <= w
+        return max(abs(ya - yb), abs(xa - xb)) <= r
+
+    def out(kind):
+        res = []
+        for a in rows:
+            keys = [b for b in range(n) if kind == "dense" or kept(kind, a, b)]
+            res.append([sum(v[b, j] for b in keys) / len(keys) for j in range(d)])
+        return res
+
+    od, osp, ot = out("dense"), out("spatial"), out("temporal")
+    cells = len(rows) * d
+    es = sum((osp[i][j] - od[i][j]) ** 2 for i in range(len(rows)) for j in range(d)) / cells
+    et = sum((ot[i][j] - od[i][j]) ** 2 for i in range(len(rows)) for j in range(d)) / cells
+    got_s, got_t, choice = oracle.route_head(q, k, vb, 0.3, g, w, r, rows)
+    assert es > 0 and et > 0
+    assert abs(got_s - es) <= 1e-12 * es and abs(got_t - et) <= 1e-12 * et, (got_s, es, got_t, et)
+    assert choice == ("temporal" if et < es else "spatial")
