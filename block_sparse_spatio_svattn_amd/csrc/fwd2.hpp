@@ -389,15 +389,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // a wave works out the row of the tile's key j once per tile, and each copy
   // takes the row of its key from that lane (a cross-lane read): one closed
   // form per lane and tile instead of one per copy.
+  // The offsets are worked out when the tile's turn in the list comes, one
+  // step before its copies go out, so the cross-lane reads land while the
+  // wave computes scores.
   static_assert(BK <= 64, "one lane per key of a tile");
   const bool gathered = GTH && hd.gather;
-  auto tile_rows = [&](int key0) __attribute__((always_inline)) -> int {
-    if constexpr (GTH) return gathered ? tm_to_fm(g, order, min(key0 + lane, N - 1)) : 0;
-    return 0;
+  uint32_t goff[GTH ? OPC : 1];  // this lane's copy offsets for the next gathered tile
+  auto gather_offsets = [&](int key0) __attribute__((always_inline)) {
+    if constexpr (GTH) {
+      const int rows = tm_to_fm(g, order, min(key0 + lane, N - 1));
+#pragma unroll
+      for (int i = 0; i < OPC; ++i) {
+        const uint32_t off = (uint32_t)dma_off[i];
+        const int row = __builtin_amdgcn_ds_bpermute((int)(off / (D * 2)) << 2, rows);
+        goff[i] = (uint32_t)row * (uint32_t)(D * 2) + off % (D * 2);
+      }
+    }
   };
   // Copy i of this wave for the tile starting at key0, into stage st (ragged:
   // the tile runs past the last token).
-  auto issue_op = [&](int i, int key0, int st, bool ragged, int rows) __attribute__((always_inline)) {
+  auto issue_op = [&](int i, int key0, int st, bool ragged) __attribute__((always_inline)) {
     const bool is_k = i < KOPS;
     const int pc = op_piece(i);
     if (cw < 0) return;
@@ -412,10 +423,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
     uint32_t off = (uint32_t)dma_off[i];
     if (gathered) {  // the row holding the key's position (the last one past N), same chunk
-      if constexpr (GTH) {
-        const int row = __builtin_amdgcn_ds_bpermute((int)(off / (D * 2)) << 2, rows);
-        off = (uint32_t)row * (uint32_t)(D * 2) + off % (D * 2);
-      }
+      if constexpr (GTH) off = goff[i];
     } else if (ragged) {  // rows past N read row N-1 (their keys are masked)
       const int row = (int)(off / (D * 2));
       off = (uint32_t)((min(key0 + row, N - 1) - key0) * (D * 2) + (off - row * (D * 2)));
@@ -431,13 +439,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   // All copies of a tile at once (one branch for a ragged tile).
   auto issue = [&](int key0, int st) __attribute__((always_inline)) {
-    const int rows = tile_rows(key0);
     if (key0 + BK > N) {
 #pragma unroll
-      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, true, rows);
+      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, true);
     } else {
 #pragma unroll
-      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, false, rows);
+      for (int i = 0; i < OPC; ++i) issue_op(i, key0, st, false);
     }
     issue_kc(key0, st);
   };
@@ -754,7 +761,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (!dma) return;
 #pragma unroll
     for (int i = 0; i < OPC; ++i)
-      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st, key0 + BK > N, 0);  // the two-group schedule never gathers
+      if ((i * NCH) / OPC == chunk) issue_op(i, key0, st, key0 + BK > N);
   };
   auto next_stage = [&](int st) __attribute__((always_inline)) { return st == STAGES - 1 ? 0 : st + 1; };
 
@@ -840,10 +847,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i <= TPB; ++i) fetch(i, wk[i], wc[i]);
     if (n > 0) {
+      if (gathered) gather_offsets(wk[0]);
       issue(wk[0], 0);
     }
     if constexpr (TPB == 2)
-      if (n > 1) issue(wk[1], 1);
+      if (n > 1) {
+        if (gathered) gather_offsets(wk[1]);
+        issue(wk[1], 1);
+      }
     wait_tiles();
     __syncthreads();
     int grp = 0;  // first stage of the current group
@@ -854,6 +865,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (u == 0 || t < n) {
           const int st = grp + u;
           fetch(t + TPB + 1, wk[TPB + 1], wc[TPB + 1]);
+          if (gathered && t + TPB < n) gather_offsets(wk[TPB]);
           // a wave whose queries keep no key of this tile skips S, softmax and P V
           uint64_t keep[QG];
           const int ms = plan(st, wk[0], wc[0], keep);
