@@ -634,3 +634,31 @@ def test_route_heads_repeat_is_deterministic(sv):
     b, _ = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, [5, 50])
     torch.cuda.synchronize()
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_route_heads_sixteen_heads_two_group_schedule(sv):
+    """16 heads: the routing forward's first launch then holds only dense
+    slots, which at 256 x 32 tiles run the two-group schedule (static grid),
+    with key splits and partial outputs; deviations equal the plain forward's
+    to 1%."""
+    heads = tuple([synth.Head("spatial", window=1)] * 16)
+    wl = synth.Workload(name="route16", seed=41, frames=4, height=8, width=16, head_dim=128, heads=heads,
+                        tiles=((256, 32),))
+    inp = synth.make_inputs(wl)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    g, sp, tp, dm, sm, tm = _route_setup(sv, wl, 1, 2, bq=256, bk=32)
+    qtiles = [0, 1]
+    err, ch = sv.route_heads(g, q, k, v, sp, tp, dm, sm, tm, scales, qtiles)
+    H = wl.n_heads
+    outs = [sv.forward(g, q, k, v, [m] * H, [mp] * H, scales)
+            for m, mp in ((sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0), dm), (sp, sm), (tp, tm))]
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(t * 256, (t + 1) * 256) for t in qtiles])
+    od, osp, ot = (f64_of(o)[:, rows] for o in outs)
+    es = ((osp - od) ** 2).mean(axis=(1, 2))
+    et = ((ot - od) ** 2).mean(axis=(1, 2))
+    err = err.cpu().numpy().astype(np.float64)
+    for h in range(H):
+        assert abs(err[h, 0] - es[h]) <= 0.01 * es[h] + 1e-9, (h, err[h], es[h])
+        assert abs(err[h, 1] - et[h]) <= 0.01 * et[h] + 1e-9, (h, err[h], et[h])
