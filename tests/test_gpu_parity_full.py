@@ -186,3 +186,67 @@ def test_headline_routing_against_oracle(sv):
         assert abs(err[h, 1] - et) <= 0.02 * et + 1e-9, (h, err[h], es, et)
         if abs(es - et) > 0.05 * max(es, et):
             assert ch[h] == (sv.TEMPORAL if choice == "temporal" else sv.SPATIAL), (h, es, et)
+
+
+def test_headline_fused_step_bit_identical(sv):
+    """The fused permutation at full size, as the benchmark times it: the
+    75,600-token, 10-head step with the temporal heads read and written in
+    place equals permute -> forward -> unpermute bit for bit."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    wl = synth.WORKLOADS["headline"]
+    inp = _inputs("headline")
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    masks = [sv_mask(h, "tmb" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    o_sep = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK)(q, k, v, scales)
+    o_fused = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK, fused=True)(q, k, v, scales)
+    torch.cuda.synchronize()
+    assert torch.equal(o_sep.view(torch.int16), o_fused.view(torch.int16))
+
+
+def test_headline_tile_aligned_sampled_qtiles(sv):
+    """The tile-aligned traversal at full size in the benchmark's launch
+    configuration (256 x 64 maps built with MAP_TILE_ALIGNED, temporal heads in
+    the blocked order): for each head, twelve q-tiles (the first, the ragged
+    last and ten seeded ones) and three rows in each against the oracle's
+    tile-snapped mask."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    wl = synth.WORKLOADS["headline"]
+    inp = _inputs("headline")
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    og = oracle.Geometry(wl.frames, wl.height, wl.width)
+    orders = ["tmb" if h.kind == synth.TEMPORAL else "fm" for h in wl.heads]
+    masks = [sv_mask(h, o) for h, o in zip(wl.heads, orders)]
+    layer = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK, map_flags=sv.MAP_TILE_ALIGNED)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    out = layer(q, k, v, scales)
+    torch.cuda.synchronize()
+    n = wl.n_tokens
+    n_qt = -(-n // BQ)
+    layouts = {o: oracle.layout_tokens(og, o) for o in set(orders)}
+    jobs = []
+    for h in range(wl.n_heads):
+        rng = np.random.Generator(np.random.PCG64(2000 + h))
+        qts = sorted({0, n_qt - 1, *rng.choice(np.arange(1, n_qt - 1), size=10, replace=False).tolist()})
+        pos = []
+        for qt in qts:
+            lo, hi = qt * BQ, min(n, (qt + 1) * BQ) - 1
+            pos.extend([lo, hi, int(rng.integers(lo, hi + 1))])
+        pos = np.unique(np.asarray(pos, dtype=np.int64))
+        jobs.append((h, layouts[orders[h]][pos]))
+    print(f"tile-aligned headline: {sum(len(t) for _, t in jobs)} rows", flush=True)
+
+    def oracle_head(job):
+        h, tok = job
+        head = wl.heads[h]
+        return oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), og, head.kind,
+                                  head.window, head.radius, rows=tok, tile_aligned=(orders[h], BQ, BK))[0]
+
+    with ThreadPoolExecutor(4) as ex:
+        refs = list(ex.map(oracle_head, jobs))
+    got = np.concatenate([f64_of(out[h][torch.from_numpy(tok).cuda()]) for h, tok in jobs])
+    want = np.concatenate(refs)
+    _report("headline/tile-aligned/tmb/12-qtiles-per-head", got, want, None)
+    assert_close(got, want, "headline tile-aligned")
