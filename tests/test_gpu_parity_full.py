@@ -250,3 +250,38 @@ def test_headline_tile_aligned_sampled_qtiles(sv):
     want = np.concatenate(refs)
     _report("headline/tile-aligned/tmb/12-qtiles-per-head", got, want, None)
     assert_close(got, want, "headline tile-aligned")
+
+
+def test_headline_dense_and_naive_comparators(sv):
+    """The benchmark's two comparators at full size: the dense launch (every
+    tile full) against the fp64 oracle's dense attention on one row per q-tile
+    of every head (the ragged last q-tile included), and the naive traversal
+    (every visited tile masked) bit-identical to the exact maps' forward."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    wl = synth.WORKLOADS["headline"]
+    inp = _inputs("headline")
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    og = oracle.Geometry(wl.frames, wl.height, wl.width)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    dense = SparseVideoAttention(g, [sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0)] * wl.n_heads, wl.head_dim, BQ, BK)
+    o_dense = dense(q, k, v, scales)
+    masks = [sv_mask(h, "tmb" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
+    o_exact = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK)(q, k, v, scales)
+    o_naive = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK, map_flags=sv.MAP_ALL_BOUNDARY)(q, k, v, scales)
+    torch.cuda.synchronize()
+    assert torch.equal(o_exact.view(torch.int16), o_naive.view(torch.int16))
+    n = wl.n_tokens
+    jobs = [(h, stratified_positions(n, BQ, seed=3000 + h, per_tile=1)) for h in range(wl.n_heads)]
+
+    def oracle_head(job):
+        h, rows = job
+        return oracle.attend_head(inp.q[h], inp.k[h], inp.v[h], float(inp.scales[h]), og, "dense", 0, 0,
+                                  rows=rows)[0]
+
+    with ThreadPoolExecutor(4) as ex:
+        refs = list(ex.map(oracle_head, jobs))
+    got = np.concatenate([f64_of(o_dense[h][torch.from_numpy(rows).cuda()]) for h, rows in jobs])
+    want = np.concatenate(refs)
+    _report("headline/dense/1-per-qtile", got, want, None)
+    assert_close(got, want, "headline dense")
