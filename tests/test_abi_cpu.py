@@ -306,6 +306,12 @@ def test_route_validation():
     # most 32) of fp32 rows and their lse, then one pair of sums per 16-row merge workgroup
     rows = heads * 2 * 32 * 64
     assert b.value == 256 + 3 * (rows * d * 4 + rows * 4) + heads * 2 * (64 // 16) * 8
+    # the split count follows the work-item target: ceil(1024 / (3 heads n_qtiles)), clamped to [1, 32]
+    for hh, dd, bq, nq, splits in [(10, 128, 256, 2, 18), (400, 128, 256, 1, 1), (1, 128, 256, 32, 11),
+                                   (3, 64, 32, 5, 23), (342, 64, 128, 1, 1), (341, 64, 128, 1, 2)]:
+        assert L.svattn_route_scratch_bytes(hh, dd, bq, nq, ctypes.byref(b)) == 0
+        r = hh * nq * splits * bq
+        assert b.value == 256 + 3 * (r * dd * 4 + r * 4) + hh * nq * (bq // (1024 // dd)) * 8, (hh, dd, bq, nq)
     assert L.svattn_route_scratch_bytes(heads, d, 64, 33, ctypes.byref(b)) == INVALID
     assert L.svattn_route_scratch_bytes(heads, 96, 64, 2, ctypes.byref(b)) == UNSUPPORTED
     sp, tp = sv.Mask(sv.SPATIAL, 0, 1, 0), sv.Mask(sv.TEMPORAL, 0, 0, 1)
