@@ -29,7 +29,8 @@ Readings where the pages are silent (each is listed in the design notes):
   or f_k == 0 (inclusive windows, clipped at grid edges, anchor on the key side);
   temporal-major order is anchor-first: frame 0 in patch order, then for each
   patch p its frames 1..F-1 (the library's blocked variant lists the patches
-  4x4 block by block instead of row by row); tile classes count only in-range pairs; masked
+  4x4 block by block instead of row by row, its strip variant in snake strips
+  two patch columns wide); tile classes count only in-range pairs; masked
   scores are -inf.
 
 Pins (tests/test_oracle_pins.py): closed-form kept counts, the pages' kept
@@ -46,6 +47,9 @@ from .core import (  # noqa: F401
     PATCH_BLOCK,
     blocked_patch_order,
     temporal_major_blocked_perm,
+    PATCH_STRIP,
+    strip_patch_order,
+    temporal_major_strips_perm,
     layout_tokens,
     keep_matrix,
     kept_count,

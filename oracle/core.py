@@ -92,15 +92,51 @@ def temporal_major_blocked_perm(g: Geometry) -> np.ndarray:
     return np.asarray(order, dtype=np.int64)
 
 
+PATCH_STRIP = 2
+
+
+def strip_patch_order(g: Geometry) -> np.ndarray:
+    """Raster patch indices listed in snake strips.
+
+    Not from the pages either (a library layout, like the blocked order): the
+    grid is cut into column strips PATCH_STRIP patches wide (the last one
+    narrower when the width does not divide), the strips are listed left to
+    right, an even-numbered strip is walked from the top patch row down and an
+    odd-numbered one from the bottom row up, and each patch row of a strip is
+    listed left to right.  Consecutive patches are then always grid neighbours,
+    also from one strip to the next.  Built by sorting the patches on (strip,
+    row in the strip's walking direction, column), not from a rank formula.
+    """
+    y, x = np.divmod(np.arange(g.patches), g.width)
+    strip = x // PATCH_STRIP
+    walk = np.where(strip % 2 == 1, g.height - 1 - y, y)
+    return np.lexsort((x, walk, strip)).astype(np.int64)  # last key is the primary one
+
+
+def temporal_major_strips_perm(g: Geometry) -> np.ndarray:
+    """perm[t'] for the anchor-first temporal-major layout over patches in
+    snake-strip order: frame 0 in that patch order, then for each patch in it
+    its frames 1..F-1."""
+    seq = strip_patch_order(g)
+    order = [int(p) for p in seq]
+    for p in seq:
+        for f in range(1, g.frames):
+            order.append(f * g.patches + int(p))
+    return np.asarray(order, dtype=np.int64)
+
+
 def layout_tokens(g: Geometry, order: str) -> np.ndarray:
     """Frame-major token id held at each position of a head's token order
-    ("fm", "tm", or "tmb" for temporal-major over blocked patches)."""
+    ("fm", "tm", "tmb" for temporal-major over blocked patches, or "tms" for
+    temporal-major over snake strips)."""
     if order == "fm":
         return np.arange(g.n, dtype=np.int64)
     if order == "tm":
         return temporal_major_perm(g)
     if order == "tmb":
         return temporal_major_blocked_perm(g)
+    if order == "tms":
+        return temporal_major_strips_perm(g)
     raise ValueError(order)
 
 

@@ -39,6 +39,7 @@ DENSE = "dense"
 FRAME_MAJOR = "fm"
 TEMPORAL_MAJOR = "tm"
 TEMPORAL_MAJOR_BLOCKED = "tmb"  # temporal-major over 4x4 patch blocks (a library layout)
+TEMPORAL_MAJOR_STRIPS = "tms"   # temporal-major over snake strips two patches wide (a library layout)
 
 
 @dataclasses.dataclass(frozen=True)

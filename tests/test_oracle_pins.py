@@ -181,6 +181,42 @@ def test_blocked_patch_order_hand_example_and_properties():
         assert (oracle.unpermute_rows(x_l, g, "tmb")[perm] == x_l).all()
 
 
+def test_strip_patch_order_hand_example_and_properties():
+    ex = _golden("strip_patch_order.json")
+    H, W = ex["geometry"]["height"], ex["geometry"]["width"]
+    assert oracle.strip_patch_order(Geometry(1, H, W)).tolist() == ex["order"]
+    tms = ex["temporal_major_strips"]
+    perm = oracle.temporal_major_strips_perm(Geometry(tms["frames"], H, W))
+    for pos, tok in tms["pairs"]:
+        assert perm[pos] == tok
+    S = oracle.PATCH_STRIP
+    for g in (Geometry(4, 8, 8), Geometry(5, 24, 40), Geometry(2, 3, 5), Geometry(1, 4, 4),
+              Geometry(3, 9, 13), Geometry(2, 1, 7), Geometry(3, 7, 1), Geometry(21, 45, 80)):
+        seq = oracle.strip_patch_order(g)
+        P = g.patches
+        assert sorted(seq.tolist()) == list(range(P))                  # bijection
+        y, x = seq // g.width, seq % g.width
+        # a snake: every patch is a grid neighbour of the one before it
+        assert (np.maximum(np.abs(np.diff(y)), np.abs(np.diff(x))) == 1).all()
+        strip = x // S
+        assert (np.diff(strip) >= 0).all()                             # strips left to right, each contiguous
+        for s_ in np.unique(strip):
+            yy, xx = y[strip == s_], x[strip == s_]
+            assert len(yy) == g.height * (min(g.width, S * s_ + S) - S * s_)   # the whole column strip
+            step = np.diff(yy)
+            assert ((step >= 0) if s_ % 2 == 0 else (step <= 0)).all()        # down, then up, ...
+        perm = oracle.temporal_major_strips_perm(g)
+        assert sorted(perm.tolist()) == list(range(g.n))
+        assert (perm[:P] == seq).all()                                 # anchor frame in front, strip order
+        if g.frames > 1:
+            runs = perm[P:].reshape(P, g.frames - 1)                   # one run of frames 1..F-1 per patch
+            f, _, _ = oracle.frame_major_coords(g)
+            assert (f[runs] == np.arange(1, g.frames)[None, :]).all()
+            assert ((runs % P) == seq[:, None]).all()
+        x_l = np.random.default_rng(2).standard_normal((g.n, 2))[perm]
+        assert (oracle.unpermute_rows(x_l, g, "tms")[perm] == x_l).all()
+
+
 def _inputs(seed, n, d, heads=1):
     q = synth.random_bf16((heads, n, d), seed)
     k = synth.random_bf16((heads, n, d), seed + 1)
@@ -254,7 +290,7 @@ def test_output_inside_kept_value_range():
         assert (o[i] >= kv.min(0) - 1e-12).all() and (o[i] <= kv.max(0) + 1e-12).all()
 
 
-@pytest.mark.parametrize("order", ["tm", "tmb"])
+@pytest.mark.parametrize("order", ["tm", "tmb", "tms"])
 @pytest.mark.parametrize("F,H,W,r", [(4, 8, 8, 1), (5, 6, 10, 2), (3, 9, 13, 2)])
 def test_permute_attend_unpermute_equals_direct(F, H, W, r, order):
     """Attention in a temporal-major order, mapped back, equals direct attention."""
@@ -262,7 +298,8 @@ def test_permute_attend_unpermute_equals_direct(F, H, W, r, order):
     q, k, v = _inputs(60, g.n, 32)
     sc = float(np.float32(0.2))
     direct, dl = oracle.attend_head(q[0], k[0], v[0], sc, g, "temporal", 0, r)
-    perm = oracle.temporal_major_perm(g) if order == "tm" else oracle.temporal_major_blocked_perm(g)
+    perm = {"tm": oracle.temporal_major_perm, "tmb": oracle.temporal_major_blocked_perm,
+            "tms": oracle.temporal_major_strips_perm}[order](g)
     Q, K, V = (oracle.bf16_to_f64(t[0])[perm] for t in (q, k, v))
     keep_tm = oracle.keep_matrix(g, "temporal", 0, r, perm, perm)
     o_tm, l_tm = oracle.attend_rows(Q, K, V, sc, keep_tm)
@@ -310,11 +347,11 @@ def _patch_ranges(g, order, a, b):
     return out
 
 
-def _patches_tmb(g, a, b):
-    """(y, x) of the patches covered by positions [a, b) of the blocked
-    temporal-major order (the order itself is pinned above)."""
+def _patches_listed(g, order, a, b):
+    """(y, x) of the patches covered by positions [a, b) of the blocked or
+    snake-strip temporal-major order (the orders themselves are pinned above)."""
     P, F = g.patches, g.frames
-    seq = oracle.blocked_patch_order(g)
+    seq = oracle.blocked_patch_order(g) if order == "tmb" else oracle.strip_patch_order(g)
     pos = np.arange(a, b)
     rank = np.where(pos < P, pos, (pos - P) // max(F - 1, 1))
     p = np.unique(seq[rank])
@@ -339,9 +376,9 @@ def _geometric_class(g, kind, w, r, order, r0, r1, c0, c1):
         c, d = _frames(g, order, n0, c1)
         near_any = max(0, a - d, c - b) <= w
         near_all = max(b - c, d - a) <= w
-    elif order == "tmb":
+    elif order in ("tmb", "tms"):
         # the rows' and non-frame-0 columns' patches, listed explicitly
-        R, C = _patches_tmb(g, r0, r1), _patches_tmb(g, n0, c1)
+        R, C = _patches_listed(g, order, r0, r1), _patches_listed(g, order, n0, c1)
         cheb = np.maximum(np.abs(R[0][:, None] - C[0][None]), np.abs(R[1][:, None] - C[1][None]))
         near_any, near_all = cheb.min() <= r, cheb.max() <= r
     else:
@@ -379,9 +416,12 @@ CASES = [
     (Geometry(4, 8, 8), "temporal", 0, 1, "tmb", 32, 32),
     (Geometry(3, 5, 7), "temporal", 0, 1, "tmb", 32, 32),     # ragged blocks and tiles
     (Geometry(3, 9, 13), "temporal", 0, 2, "tmb", 32, 64),
+    (Geometry(4, 8, 8), "temporal", 0, 1, "tms", 32, 32),
+    (Geometry(3, 5, 7), "temporal", 0, 1, "tms", 32, 32),     # odd width: a last strip one patch wide
+    (Geometry(3, 9, 13), "temporal", 0, 2, "tms", 32, 64),
 ] + [(Geometry(5, 24, 40), kind, w, r, order, bq, bk)
      for (kind, w, r, order) in [("spatial", 1, 0, "fm"), ("temporal", 0, 2, "fm"), ("temporal", 0, 2, "tm"),
-                                 ("temporal", 0, 2, "tmb")]
+                                 ("temporal", 0, 2, "tmb"), ("temporal", 0, 2, "tms")]
      for bq in (64, 128) for bk in (64, 128)]
 
 
@@ -413,7 +453,8 @@ def test_spatial_frame_aligned_tiles_are_never_boundary():
 
 
 @pytest.mark.parametrize("kind,w,r,order", [("spatial", 1, 0, "fm"), ("temporal", 0, 31, "tm"),
-                                            ("temporal", 0, 31, "fm"), ("temporal", 0, 31, "tmb")])
+                                            ("temporal", 0, 31, "fm"), ("temporal", 0, 31, "tmb"),
+                                            ("temporal", 0, 31, "tms")])
 def test_headline_tile_rows_match_geometry(kind, w, r, order):
     g = Geometry(21, 45, 80)
     qtiles = [0, 14, 15, 150, 295]
