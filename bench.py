@@ -15,11 +15,12 @@ Prints one JSON line.  `value` is effective TFLOP/s of the whole step
 `roofline` is for the dominant kernel (the attention forward), timed with
 HIP events on the stream it is launched on.
 
-    python bench.py [--steps K] [--warmup W] [--workload headline] [--temporal-order tmb|tm|fm]
+    python bench.py [--steps K] [--warmup W] [--workload headline] [--temporal-order tms|tmb|tm|fm]
 
-Temporal heads run by default in the temporal-major order over 4x4 patch
-blocks (the library's layout; the pages' temporal-major order lists patches
-row by row and is timed beside it as `other_temporal_order`).
+Temporal heads run by default in the temporal-major order over snake strips
+of two patch columns (the library's layout); the pages' temporal-major order,
+which lists patches row by row, and the one over 4x4 patch blocks are timed
+beside it as `other_temporal_orders`.
 """
 from __future__ import annotations
 
@@ -79,9 +80,9 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--block-q", type=int, default=256)
     ap.add_argument("--block-k", type=int, default=64)
-    ap.add_argument("--temporal-order", choices=["tm", "tmb", "fm"], default="tmb",
+    ap.add_argument("--temporal-order", choices=["tm", "tmb", "tms", "fm"], default="tms",
                     help="token order of the temporal heads: temporal-major (patches in raster order), "
-                         "temporal-major over 4x4 patch blocks, or frame-major")
+                         "temporal-major over 4x4 patch blocks or over snake strips, or frame-major")
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
@@ -89,7 +90,7 @@ def main():
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-permutation step")
     ap.add_argument("--no-routing", action="store_true", help="skip the head-routing timing")
     ap.add_argument("--no-alt-order", action="store_true",
-                    help="skip the forward with the temporal heads in the other temporal-major order")
+                    help="skip the forwards with the temporal heads in the other temporal-major orders")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the GPU clock sample taken under load")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -110,6 +111,8 @@ def main():
     from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
     import svattn_synth as synth
 
+    ORDER_CODES = {"tm": sv.TEMPORAL_MAJOR, "tmb": sv.TEMPORAL_MAJOR_BLOCKED, "tms": sv.TEMPORAL_MAJOR_STRIPS,
+                   "fm": sv.FRAME_MAJOR}
     wl = synth.WORKLOADS[args.workload]
     g = sv.Geom(wl.frames, wl.height, wl.width)
     kinds = {synth.SPATIAL: sv.SPATIAL, synth.TEMPORAL: sv.TEMPORAL, synth.DENSE: sv.DENSE}
@@ -117,7 +120,7 @@ def main():
     for h in wl.heads:
         order = sv.FRAME_MAJOR
         if h.kind == synth.TEMPORAL:
-            order = {"tm": sv.TEMPORAL_MAJOR, "tmb": sv.TEMPORAL_MAJOR_BLOCKED, "fm": sv.FRAME_MAJOR}[args.temporal_order]
+            order = ORDER_CODES[args.temporal_order]
         masks.append(sv.Mask(kinds[h.kind], order, h.window, h.radius))
     H, N, D = wl.n_heads, wl.n_tokens, wl.head_dim
 
@@ -199,10 +202,11 @@ def main():
     peak = metrics.BF16_PEAK_TFLOPS
 
     extra = {}
-    # ---- the other temporal-major order (patches in raster order vs 4x4 blocks) ----
-    if not args.no_alt_order and args.temporal_order in ("tm", "tmb"):
-        alt = "tm" if args.temporal_order == "tmb" else "tmb"
-        alt_order = sv.TEMPORAL_MAJOR if alt == "tm" else sv.TEMPORAL_MAJOR_BLOCKED
+    # ---- the other temporal-major orders (patches row by row, 4x4 blocks, snake strips) ----
+    alts = [] if args.no_alt_order or args.temporal_order == "fm" else \
+        [o for o in ("tm", "tmb", "tms") if o != args.temporal_order]
+    for alt in alts:
+        alt_order = ORDER_CODES[alt]
         amasks = [sv.Mask(m.kind, alt_order if m.order != sv.FRAME_MAJOR else m.order, m.window, m.radius)
                   for m in masks]
         alayer = SparseVideoAttention(g, amasks, D, args.block_q, args.block_k)
@@ -221,8 +225,8 @@ def main():
         alt_ms = float(np.mean([a.elapsed_time(b) for a, b in am]))
         anz = {str((m.kind, m.order, m.window, m.radius)): mp.nnz() for m, mp in zip(alayer.masks, alayer.maps)}
         log(f"forward with temporal heads in order {alt}: {alt_ms:.3f} ms; nnz {anz}")
-        extra["other_temporal_order"] = {"order": alt, "ms": round(alt_ms, 4),
-                                         "forward_ms_ratio": round(alt_ms / fwd_ms, 3)}
+        extra.setdefault("other_temporal_orders", []).append(
+            {"order": alt, "ms": round(alt_ms, 4), "forward_ms_ratio": round(alt_ms / fwd_ms, 3)})
         del alayer, aout
     # ---- dense comparator: the same kernel, every tile full ----
     if not args.no_dense:

@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "SPATIAL", "TEMPORAL", "DENSE", "FRAME_MAJOR", "TEMPORAL_MAJOR", "TEMPORAL_MAJOR_BLOCKED", "PATCH_BLOCK",
+    "TEMPORAL_MAJOR_STRIPS", "PATCH_STRIP",
     "TILE_EMPTY", "TILE_BOUNDARY", "TILE_FULL", "MAP_ALL_BOUNDARY", "MAP_TILE_ALIGNED", "FORWARD_WORKSPACE_BYTES",
     "new_workspace", "forward_fused", "route_heads", "route_scratch_bytes",
     "SvattnError", "Geom", "Mask", "TileMap", "lib", "version",
@@ -29,8 +30,9 @@ __all__ = [
 ]
 
 SPATIAL, TEMPORAL, DENSE = 0, 1, 2
-FRAME_MAJOR, TEMPORAL_MAJOR, TEMPORAL_MAJOR_BLOCKED = 0, 1, 2
+FRAME_MAJOR, TEMPORAL_MAJOR, TEMPORAL_MAJOR_BLOCKED, TEMPORAL_MAJOR_STRIPS = 0, 1, 2, 3
 PATCH_BLOCK = 4  # SVATTN_PATCH_BLOCK: patches per block side in TEMPORAL_MAJOR_BLOCKED
+PATCH_STRIP = 2  # SVATTN_PATCH_STRIP: patch columns per strip in TEMPORAL_MAJOR_STRIPS
 TILE_EMPTY, TILE_BOUNDARY, TILE_FULL = 0, 1, 2
 MAP_ALL_BOUNDARY = 1
 MAP_TILE_ALIGNED = 2
@@ -225,8 +227,8 @@ def _permute(geom, x, out, stream, order, to_tm, what):
 
 
 def permute_tokens(geom: Geom, x: torch.Tensor, out=None, stream=None, order: int = TEMPORAL_MAJOR) -> torch.Tensor:
-    """Frame-major -> temporal-major rows (anchor-first; `order` TEMPORAL_MAJOR
-    or TEMPORAL_MAJOR_BLOCKED) of a [heads, N, d] bf16 tensor."""
+    """Frame-major -> temporal-major rows (anchor-first; `order` TEMPORAL_MAJOR,
+    TEMPORAL_MAJOR_BLOCKED or TEMPORAL_MAJOR_STRIPS) of a [heads, N, d] bf16 tensor."""
     return _permute(geom, x, out, stream, order, True, "svattn_permute_tokens")
 
 

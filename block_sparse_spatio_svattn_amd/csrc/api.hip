@@ -58,9 +58,9 @@ int check_mask(const svattn_mask* m) {
   if (!m) return fail(SVATTN_ERR_INVALID_ARG, "mask is NULL");
   if (m->kind < SVATTN_SPATIAL || m->kind > SVATTN_DENSE)
     return fail(SVATTN_ERR_INVALID_ARG, "mask kind %d is not SPATIAL/TEMPORAL/DENSE", m->kind);
-  if (m->order != SVATTN_FRAME_MAJOR && m->order != SVATTN_TEMPORAL_MAJOR &&
-      m->order != SVATTN_TEMPORAL_MAJOR_BLOCKED)
-    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not FRAME_MAJOR/TEMPORAL_MAJOR/TEMPORAL_MAJOR_BLOCKED",
+  if (m->order != SVATTN_FRAME_MAJOR && !is_temporal_major(m->order))
+    return fail(SVATTN_ERR_INVALID_ARG,
+                "token order %d is not FRAME_MAJOR / TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED / TEMPORAL_MAJOR_STRIPS",
                 m->order);
   if (m->window < 0 || m->radius < 0)
     return fail(SVATTN_ERR_INVALID_ARG, "window %d / radius %d must be >= 0", m->window, m->radius);
@@ -229,8 +229,9 @@ int svattn_permutation_index_order(const svattn_geom* geom, int32_t order, int32
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
-  if (order != SVATTN_FRAME_MAJOR && order != SVATTN_TEMPORAL_MAJOR && order != SVATTN_TEMPORAL_MAJOR_BLOCKED)
-    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not FRAME_MAJOR / TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED",
+  if (order != SVATTN_FRAME_MAJOR && !is_temporal_major(order))
+    return fail(SVATTN_ERR_INVALID_ARG,
+                "token order %d is not FRAME_MAJOR / TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED / TEMPORAL_MAJOR_STRIPS",
                 order);
   if (!perm) return fail(SVATTN_ERR_INVALID_ARG, "perm is NULL");
   if (!aligned(perm, 4) || (inv && !aligned(inv, 4)))
@@ -246,8 +247,9 @@ static int permute_common(const svattn_geom* geom, int32_t order, int32_t heads,
   int64_t n;
   int s = check_geom(geom, &n);
   if (s) return s;
-  if (order != SVATTN_TEMPORAL_MAJOR && order != SVATTN_TEMPORAL_MAJOR_BLOCKED)
-    return fail(SVATTN_ERR_INVALID_ARG, "token order %d is not TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED", order);
+  if (!is_temporal_major(order))
+    return fail(SVATTN_ERR_INVALID_ARG,
+                "token order %d is not TEMPORAL_MAJOR / TEMPORAL_MAJOR_BLOCKED / TEMPORAL_MAJOR_STRIPS", order);
   if (heads < 1) return fail(SVATTN_ERR_INVALID_ARG, "heads = %d must be >= 1", heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(SVATTN_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);

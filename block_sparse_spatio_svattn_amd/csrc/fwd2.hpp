@@ -582,6 +582,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             int ry, rx;
             if (order == SVATTN_TEMPORAL_MAJOR_BLOCKED) {
               blocked_yx(g, pr, ry, rx);
+            } else if (order == SVATTN_TEMPORAL_MAJOR_STRIPS) {
+              strips_yx(g, pr, ry, rx);
             } else {
               ry = (int)g.divW.div((uint32_t)pr);
               rx = pr - ry * g.W;

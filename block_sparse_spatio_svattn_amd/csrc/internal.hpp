@@ -43,10 +43,16 @@ struct Geo {
   // block row has HL rows, the last block column WL columns.
   int32_t NBR, NBC, HL, WL;
   FastDiv divBW, divBHL, divWL;  // by B*W, B*HL and WL
+  // Snake-strip patch order (S = SVATTN_PATCH_STRIP): NS column strips, the
+  // last one WS columns wide.
+  int32_t NS, WS;
+  FastDiv divSH;  // by S*H
 };
 
 constexpr int kPatchBlock = SVATTN_PATCH_BLOCK;
 static_assert(kPatchBlock == 4, "block arithmetic below uses shifts by 2 and 4");
+constexpr int kPatchStrip = SVATTN_PATCH_STRIP;
+static_assert(kPatchStrip == 2, "strip arithmetic below uses shifts by 1");
 
 inline Geo make_geo(const svattn_geom& g) {
   Geo o;
@@ -65,6 +71,9 @@ inline Geo make_geo(const svattn_geom& g) {
   o.divBW = FastDiv((uint32_t)(kPatchBlock * o.W));
   o.divBHL = FastDiv((uint32_t)(kPatchBlock * o.HL));
   o.divWL = FastDiv((uint32_t)o.WL);
+  o.NS = (o.W + kPatchStrip - 1) / kPatchStrip;
+  o.WS = o.W - (o.NS - 1) * kPatchStrip;
+  o.divSH = FastDiv((uint32_t)(kPatchStrip * o.H));
   return o;
 }
 
@@ -101,6 +110,52 @@ __host__ __device__ __forceinline__ int blocked_rank(const Geo& g, int p) {
   return tr * kPatchBlock * g.W + tc * kPatchBlock * h + (y - tr * kPatchBlock) * w + (x - tc * kPatchBlock);
 }
 
+// Patch row and column of the patch with rank r in the snake-strip order:
+// strip s holds ranks [s*S*H, (s+1)*S*H) (fewer in a narrower last strip),
+// listed row by row with w = S columns (WS in the last strip); rows run down
+// in even strips and up in odd ones.
+__host__ __device__ __forceinline__ void strips_yx(const Geo& g, int r, int& y, int& x) {
+  const uint32_t s = g.divSH.div((uint32_t)r);
+  const uint32_t rem = (uint32_t)r - s * (uint32_t)(kPatchStrip * g.H);
+  const bool one = (int)s == g.NS - 1 && g.WS == 1;  // a last strip one column wide
+  const uint32_t iy = one ? rem : rem >> 1;
+  const uint32_t ix = rem - (one ? iy : iy << 1);
+  y = (s & 1u) ? g.H - 1 - (int)iy : (int)iy;
+  x = (int)(s * kPatchStrip + ix);
+}
+
+// Rank in the snake-strip order of raster patch p.
+__host__ __device__ __forceinline__ int strips_rank(const Geo& g, int p) {
+  const int y = (int)g.divW.div((uint32_t)p), x = p - y * g.W;
+  const int s = x >> 1;
+  const int w = s == g.NS - 1 ? g.WS : kPatchStrip;
+  const int iy = (s & 1) ? g.H - 1 - y : y;
+  return s * kPatchStrip * g.H + iy * w + (x - s * kPatchStrip);
+}
+
+// Raster patch index of rank r in the patch sequence of a temporal-major
+// order, and its inverse.
+__host__ __device__ __forceinline__ int order_patch(const Geo& g, int order, int r) {
+  if (order == SVATTN_TEMPORAL_MAJOR_BLOCKED) return blocked_patch(g, r);
+  if (order == SVATTN_TEMPORAL_MAJOR_STRIPS) {
+    int y, x;
+    strips_yx(g, r, y, x);
+    return y * g.W + x;
+  }
+  return r;
+}
+__host__ __device__ __forceinline__ int order_rank(const Geo& g, int order, int p) {
+  if (order == SVATTN_TEMPORAL_MAJOR_BLOCKED) return blocked_rank(g, p);
+  if (order == SVATTN_TEMPORAL_MAJOR_STRIPS) return strips_rank(g, p);
+  return p;
+}
+
+// The three temporal-major orders.
+__host__ __device__ __forceinline__ bool is_temporal_major(int order) {
+  return order == SVATTN_TEMPORAL_MAJOR || order == SVATTN_TEMPORAL_MAJOR_BLOCKED ||
+         order == SVATTN_TEMPORAL_MAJOR_STRIPS;
+}
+
 // Rank (in the order's patch sequence) of the patch at position t of a
 // temporal-major order.
 __host__ __device__ __forceinline__ int tm_rank(const Geo& g, int t) {
@@ -108,11 +163,10 @@ __host__ __device__ __forceinline__ int tm_rank(const Geo& g, int t) {
 }
 
 // Patch index of a token position in a given order (frame-major, or one of
-// the two anchor-first temporal-major orders).
+// the anchor-first temporal-major orders).
 __host__ __device__ __forceinline__ int patch_of(const Geo& g, int order, int t) {
   if (order == SVATTN_FRAME_MAJOR) return (int)g.divP.mod((uint32_t)t);
-  const int r = tm_rank(g, t);
-  return order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? blocked_patch(g, r) : r;
+  return order_patch(g, order, tm_rank(g, t));
 }
 
 // Frame-major token stored at position tp of a temporal-major order (perm[tp]).
@@ -123,7 +177,7 @@ __host__ __device__ __forceinline__ int tm_to_fm(const Geo& g, int order, int tp
     r = g.divF1.div(u);
     f = 1 + (u - r * g.divF1.d);
   }
-  const uint32_t p = order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? (uint32_t)blocked_patch(g, (int)r) : r;
+  const uint32_t p = (uint32_t)order_patch(g, order, (int)r);
   return (int)(f * (uint32_t)g.P + p);
 }
 
@@ -131,7 +185,7 @@ __host__ __device__ __forceinline__ int tm_to_fm(const Geo& g, int order, int tp
 __host__ __device__ __forceinline__ int fm_to_tm(const Geo& g, int order, int t) {
   const uint32_t f = g.divP.div((uint32_t)t);
   const uint32_t p = (uint32_t)t - f * (uint32_t)g.P;
-  const uint32_t r = order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? (uint32_t)blocked_rank(g, (int)p) : p;
+  const uint32_t r = (uint32_t)order_rank(g, order, (int)p);
   if (f == 0) return (int)r;
   return (int)((uint32_t)g.P + r * (uint32_t)(g.F - 1) + (f - 1));
 }

@@ -15,7 +15,9 @@
 // patch indices is at most three grid rectangles, a range of the blocked
 // patch order at most seven (the tail of its first block, whole blocks to the
 // end of that block row, whole block rows, whole blocks from the start of the
-// last block row, the head of its last block).  Between two rectangles the
+// last block row, the head of its last block), a range of the snake-strip
+// order at most seven (the tail of its first strip, whole strips, the head of
+// its last strip; a strip's rows reversed when it runs upwards).  Between two rectangles the
 // smallest Chebyshev distance is max(gap_y, gap_x) and the largest is
 // max(span_y, span_x).  Key positions below P (frame 0, the anchor) are kept
 // for every query in every order.
@@ -124,6 +126,40 @@ __host__ __device__ int blocked_rects(const Geo& g, int2 r, Rect* out) {
   return n;
 }
 
+// Rectangles of in-strip indices [i0, i1] of strip s of the snake-strip
+// order: rows of w patches, index i at walking row i / w, column i % w; the
+// walking row is the grid row in an even strip and H-1 minus it in an odd one.
+__host__ __device__ int strip_part(const Geo& g, int s, int i0, int i1, Rect* out) {
+  const int w = s == g.NS - 1 ? g.WS : kPatchStrip, x0 = s * kPatchStrip;
+  const int ya = i0 / w, xa = i0 - ya * w, yb = i1 / w, xb = i1 - yb * w;
+  int n = 0;
+  if (ya == yb) {
+    out[n++] = Rect{ya, ya, x0 + xa, x0 + xb};
+  } else {
+    out[n++] = Rect{ya, ya, x0 + xa, x0 + w - 1};
+    out[n++] = Rect{yb, yb, x0, x0 + xb};
+    if (yb > ya + 1) out[n++] = Rect{ya + 1, yb - 1, x0, x0 + w - 1};
+  }
+  if (s & 1)
+    for (int i = 0; i < n; ++i) out[i] = Rect{g.H - 1 - out[i].y1, g.H - 1 - out[i].y0, out[i].x0, out[i].x1};
+  return n;
+}
+
+// Rectangles of ranks [r.x, r.y] of the snake-strip patch order.
+__host__ __device__ int strips_rects(const Geo& g, int2 r, Rect* out) {
+  const int sh = kPatchStrip * g.H;
+  const int sa = (int)g.divSH.div((uint32_t)r.x), sb = (int)g.divSH.div((uint32_t)r.y);
+  const int ia = r.x - sa * sh, ib = r.y - sb * sh;
+  if (sa == sb) return strip_part(g, sa, ia, ib, out);
+  const int wa = sa == g.NS - 1 ? g.WS : kPatchStrip;
+  int n = 0;
+  n += strip_part(g, sa, ia, wa * g.H - 1, out + n);  // tail of the first strip
+  n += strip_part(g, sb, 0, ib, out + n);             // head of the last strip
+  if (sb > sa + 1)                                    // whole strips between
+    out[n++] = Rect{0, g.H - 1, (sa + 1) * kPatchStrip, sb * kPatchStrip - 1};
+  return n;
+}
+
 constexpr int kMaxRects = 2 * 9;  // two ranges of at most 3 + 3 + 3 rectangles
 
 __host__ __device__ int rect_set(const Geo& g, int order, int a, int b, Rect out[kMaxRects]) {
@@ -131,7 +167,9 @@ __host__ __device__ int rect_set(const Geo& g, int order, int a, int b, Rect out
   int nr = patch_ranges(g, order, a, b, rg);
   int n = 0;
   for (int i = 0; i < nr; ++i)
-    n += order == SVATTN_TEMPORAL_MAJOR_BLOCKED ? blocked_rects(g, rg[i], out + n) : rects_of(g, rg[i], out + n);
+    n += order == SVATTN_TEMPORAL_MAJOR_BLOCKED  ? blocked_rects(g, rg[i], out + n)
+         : order == SVATTN_TEMPORAL_MAJOR_STRIPS ? strips_rects(g, rg[i], out + n)
+                                                 : rects_of(g, rg[i], out + n);
   return n;
 }
 

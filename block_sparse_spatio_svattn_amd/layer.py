@@ -45,7 +45,7 @@ class SparseVideoAttention:
             if key not in cache:
                 cache[key] = build_tile_map(geom, m, block_q, block_k, device=device, flags=map_flags)
             self.maps.append(cache[key])
-        # heads stored in a temporal-major order (raster or blocked patches)
+        # heads stored in a temporal-major order (raster, blocked or strip patches)
         self.tm_heads = [h for h, m in enumerate(self.masks) if m.order != FRAME_MAJOR]
         self.tm_runs = _runs(self.tm_heads, key=lambda h: self.masks[h].order)
         self._slot = {h: i for i, h in enumerate(self.tm_heads)}

@@ -73,6 +73,19 @@ extern "C" {
  * head's tiles are fewer and less often BOUNDARY.  TEMPORAL and DENSE heads. */
 #define SVATTN_TEMPORAL_MAJOR_BLOCKED 2
 #define SVATTN_PATCH_BLOCK 4
+/* Anchor-first temporal-major over patches listed in snake strips: the patch
+ * grid is cut into column strips SVATTN_PATCH_STRIP patches wide (the last
+ * strip narrower when W is odd), strips left to right, strip 0, 2, 4, ...
+ * walked from patch row 0 down and strip 1, 3, ... from row H-1 up, each row
+ * of a strip left to right.  Frame 0 comes first in that patch order, then
+ * each patch (same order) brings its frames 1..F-1.  Also a library layout:
+ * a q-tile then covers a patch region about two columns wide, and
+ * consecutive patches are always grid neighbours, so a temporal head visits
+ * fewer tiles, and fewer BOUNDARY ones, than with 4x4 blocks (the boundary
+ * of a radius-r mask on a grid wider than tall runs mostly along columns).
+ * TEMPORAL and DENSE heads. */
+#define SVATTN_TEMPORAL_MAJOR_STRIPS 3
+#define SVATTN_PATCH_STRIP 2
 
 /* Tile classes stored in svattn_tile_map.cls / col_cls. */
 #define SVATTN_TILE_EMPTY 0
@@ -98,7 +111,8 @@ typedef struct {
 
 typedef struct {
   int32_t kind;   /* SVATTN_SPATIAL / SVATTN_TEMPORAL / SVATTN_DENSE */
-  int32_t order;  /* SVATTN_FRAME_MAJOR / SVATTN_TEMPORAL_MAJOR / SVATTN_TEMPORAL_MAJOR_BLOCKED */
+  int32_t order;  /* SVATTN_FRAME_MAJOR / SVATTN_TEMPORAL_MAJOR / SVATTN_TEMPORAL_MAJOR_BLOCKED /
+                     SVATTN_TEMPORAL_MAJOR_STRIPS */
   int32_t window; /* spatial frame window w >= 0 (inclusive) */
   int32_t radius; /* temporal Chebyshev patch radius r >= 0 (inclusive) */
 } svattn_mask;
@@ -157,7 +171,8 @@ SVATTN_API int svattn_build_tile_map_ex(const svattn_geom* geom, const svattn_ma
  */
 SVATTN_API int svattn_permutation_index(const svattn_geom* geom, int32_t* perm, int32_t* inv, void* stream);
 /* The same for any token order: SVATTN_TEMPORAL_MAJOR (as above),
- * SVATTN_TEMPORAL_MAJOR_BLOCKED, or SVATTN_FRAME_MAJOR (the identity).
+ * SVATTN_TEMPORAL_MAJOR_BLOCKED, SVATTN_TEMPORAL_MAJOR_STRIPS, or
+ * SVATTN_FRAME_MAJOR (the identity).
  * SVATTN_ERR_INVALID_ARG for another order. */
 SVATTN_API int svattn_permutation_index_order(const svattn_geom* geom, int32_t order, int32_t* perm,
                                               int32_t* inv, void* stream);
@@ -182,8 +197,8 @@ SVATTN_API int svattn_permute_tokens(const svattn_geom* geom, int32_t heads, int
 SVATTN_API int svattn_unpermute(const svattn_geom* geom, int32_t heads, int32_t head_dim,
                      const void* src, void* dst, void* stream);
 /* The same between frame-major and the temporal-major order `order`
- * (SVATTN_TEMPORAL_MAJOR or SVATTN_TEMPORAL_MAJOR_BLOCKED; another order is
- * SVATTN_ERR_INVALID_ARG): dst[h, t', :] = src[h, perm[t'], :] with perm from
+ * (SVATTN_TEMPORAL_MAJOR, SVATTN_TEMPORAL_MAJOR_BLOCKED or
+ * SVATTN_TEMPORAL_MAJOR_STRIPS; another order is SVATTN_ERR_INVALID_ARG): dst[h, t', :] = src[h, perm[t'], :] with perm from
  * svattn_permutation_index_order, and its inverse. */
 SVATTN_API int svattn_permute_tokens_order(const svattn_geom* geom, int32_t order, int32_t heads,
                                            int32_t head_dim, const void* src, void* dst, void* stream);
@@ -268,8 +283,9 @@ SVATTN_API int svattn_forward_ptrs(const svattn_geom* geom, int32_t heads, int32
  * "Co się zmieniło?", item 5, without the separate reordering passes): Q, K,
  * V, O (and lse) of every head stay in frame-major order ([heads, N,
  * head_dim] as for svattn_forward), and a head whose mask has a
- * temporal-major order (TEMPORAL_MAJOR or TEMPORAL_MAJOR_BLOCKED, its map
- * built for that order; heads may use either) is computed in that order: the
+ * temporal-major order (TEMPORAL_MAJOR, TEMPORAL_MAJOR_BLOCKED or
+ * TEMPORAL_MAJOR_STRIPS, its map built for that order; heads may mix them) is
+ * computed in that order: the
  * kernel reads the row holding each position, which is a closed form of the
  * geometry (the permutation svattn_permutation_index_order writes), and
  * writes its O and lse rows back the same way.  The result equals

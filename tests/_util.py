@@ -27,7 +27,8 @@ def sv_mask(head: synth.Head, order=None):
     kind = {synth.SPATIAL: sv.SPATIAL, synth.TEMPORAL: sv.TEMPORAL, synth.DENSE: sv.DENSE}[head.kind]
     o = head.order if order is None else order
     orders = {synth.FRAME_MAJOR: sv.FRAME_MAJOR, synth.TEMPORAL_MAJOR: sv.TEMPORAL_MAJOR,
-              synth.TEMPORAL_MAJOR_BLOCKED: sv.TEMPORAL_MAJOR_BLOCKED}
+              synth.TEMPORAL_MAJOR_BLOCKED: sv.TEMPORAL_MAJOR_BLOCKED,
+              synth.TEMPORAL_MAJOR_STRIPS: sv.TEMPORAL_MAJOR_STRIPS}
     return sv.Mask(kind, orders[o], head.window, head.radius)
 
 

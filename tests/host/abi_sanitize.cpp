@@ -135,8 +135,8 @@ int main() {
   expect(svattn_permute_tokens(&g, 2, 96, fake(0), fake(1), nullptr), SVATTN_ERR_UNSUPPORTED, "permute: d96");
   expect(svattn_unpermute(&g, 2, 64, fake(0), (char*)fake(0) + 64, nullptr), SVATTN_ERR_INVALID_ARG,
          "unpermute: overlap");
-  expect(svattn_permutation_index_order(&g, 3, (int32_t*)fake(0), nullptr, nullptr), SVATTN_ERR_INVALID_ARG,
-         "perm index: order 3");
+  expect(svattn_permutation_index_order(&g, 4, (int32_t*)fake(0), nullptr, nullptr), SVATTN_ERR_INVALID_ARG,
+         "perm index: order 4");
 
   const int H = 20;  // more heads than one launch takes
   std::vector<svattn_mask> masks(H);
@@ -169,6 +169,10 @@ int main() {
            SVATTN_OK, "perm index: valid");
     expect(svattn_permute_tokens_order(&g, SVATTN_TEMPORAL_MAJOR_BLOCKED, H, 128, fake(0), fake(1), nullptr),
            SVATTN_OK, "permute: valid");
+    const svattn_mask ts{SVATTN_TEMPORAL, SVATTN_TEMPORAL_MAJOR_STRIPS, 0, 2};
+    expect(svattn_build_tile_map(&g, &ts, &m, nullptr), SVATTN_OK, "map: valid, strip order");
+    expect(svattn_permute_tokens_order(&g, SVATTN_TEMPORAL_MAJOR_STRIPS, H, 128, fake(0), fake(1), nullptr),
+           SVATTN_OK, "permute: valid, strip order");
     const int before = svattn::g_fwd_launches;
     expect(svattn_forward(&g, H, 128, masks.data(), maps.data(), scales.data(), fake(0), fake(1), fake(2), fake(3),
                           (float*)fake(4), nullptr, nullptr),

@@ -114,10 +114,11 @@ def test_build_tile_map_validation():
     good_mask = sv.Mask(sv.TEMPORAL, sv.TEMPORAL_MAJOR, 0, 2)
     cases = [
         (sv.Mask(7, 0, 0, 0), _map(g, 64, 64), 0, INVALID),                     # bad kind
-        (sv.Mask(0, 3, 0, 0), _map(g, 64, 64), 0, INVALID),                     # bad order
+        (sv.Mask(0, 4, 0, 0), _map(g, 64, 64), 0, INVALID),                     # bad order
         (sv.Mask(0, 0, -1, 0), _map(g, 64, 64), 0, INVALID),                    # negative window
         (sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR, 1, 0), _map(g, 64, 64), 0, UNSUPPORTED),
         (sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR_BLOCKED, 1, 0), _map(g, 64, 64), 0, UNSUPPORTED),
+        (sv.Mask(sv.SPATIAL, sv.TEMPORAL_MAJOR_STRIPS, 1, 0), _map(g, 64, 64), 0, UNSUPPORTED),
         (good_mask, _map(g, 96, 64), 0, UNSUPPORTED),                           # bad block_q
         (good_mask, _map(g, 64, 64, n_qt=3), 0, INVALID),                       # wrong dims
         (good_mask, _map(g, 64, 64, col=None), 0, INVALID),                     # NULL buffer
@@ -143,15 +144,21 @@ def test_permute_validation():
     assert L.svattn_permutation_index(ctypes.byref(g), None, None, None) == INVALID
     assert L.svattn_permutation_index(ctypes.byref(g), FAKE, FAKE + 4, None) == INVALID  # perm/inv overlap
     # order-aware entries: frame-major cannot be permuted to, unknown orders are rejected
-    for o in (sv.FRAME_MAJOR, 3, -1):
+    for o in (sv.FRAME_MAJOR, 4, -1):
         assert L.svattn_permute_tokens_order(ctypes.byref(g), o, 2, 64, FAKE, FAKE * 4, None) == INVALID
         assert "order" in _err()
         assert L.svattn_unpermute_order(ctypes.byref(g), o, 2, 64, FAKE, FAKE * 4, None) == INVALID
-    assert L.svattn_permutation_index_order(ctypes.byref(g), 3, FAKE, None, None) == INVALID
+    assert L.svattn_permutation_index_order(ctypes.byref(g), 4, FAKE, None, None) == INVALID
     assert L.svattn_permute_tokens_order(ctypes.byref(g), sv.TEMPORAL_MAJOR_BLOCKED, 2, 96, FAKE, FAKE * 4,
                                          None) == UNSUPPORTED
     assert L.svattn_unpermute_order(ctypes.byref(g), sv.TEMPORAL_MAJOR_BLOCKED, 2, 64, FAKE, FAKE + 64,
                                     None) == INVALID   # overlap
+    # the strip order passes the order check and reaches the later ones
+    assert L.svattn_permute_tokens_order(ctypes.byref(g), sv.TEMPORAL_MAJOR_STRIPS, 2, 96, FAKE, FAKE * 4,
+                                         None) == UNSUPPORTED
+    assert L.svattn_unpermute_order(ctypes.byref(g), sv.TEMPORAL_MAJOR_STRIPS, 2, 64, FAKE, FAKE + 64,
+                                    None) == INVALID   # overlap
+    assert "overlap" in _err()
 
 
 def _fwd(L, g, heads=2, d=128, masks=None, maps=None, scales=None, q=FAKE, k=FAKE * 16, v=FAKE * 32,

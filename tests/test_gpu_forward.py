@@ -45,7 +45,7 @@ def _run_layer(sv, wl, inp, bq, bk, orders=None, flags=0):
 
 
 @pytest.mark.parametrize("bq,bk", [(32, 32), (64, 32), (32, 64), (256, 64), (128, 64)])
-@pytest.mark.parametrize("order", ["fm", "tm", "tmb"])
+@pytest.mark.parametrize("order", ["fm", "tm", "tmb", "tms"])
 def test_tiny_all_rows(sv, bq, bk, order):
     wl = synth.WORKLOADS["tiny"]
     inp = synth.make_inputs(wl)
@@ -66,16 +66,17 @@ def test_small_all_rows(sv, bq, bk):
 
 
 @pytest.mark.parametrize("bq,bk", [(64, 64), (256, 64), (128, 32)])
-def test_small_blocked_order_all_rows(sv, bq, bk):
-    """Temporal heads in the temporal-major order over 4x4 patch blocks
-    (24 x 40 patches: whole blocks), every output row."""
+@pytest.mark.parametrize("order", ["tmb", "tms"])
+def test_small_blocked_order_all_rows(sv, bq, bk, order):
+    """Temporal heads in the temporal-major order over 4x4 patch blocks or
+    snake strips (24 x 40 patches: whole blocks and strips), every output row."""
     wl = synth.WORKLOADS["small"]
     inp = synth.make_inputs(wl)
-    orders = ["tmb" if h.kind == synth.TEMPORAL else h.order for h in wl.heads]
+    orders = [order if h.kind == synth.TEMPORAL else h.order for h in wl.heads]
     o = _run_layer(sv, wl, inp, bq, bk, orders=orders)
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
     for h in range(wl.n_heads):
-        assert_close(f64_of(o[h]), ref[h][0], f"small tmb h{h} {bq}x{bk}")
+        assert_close(f64_of(o[h]), ref[h][0], f"small {order} h{h} {bq}x{bk}")
 
 
 def test_small_lse_and_direct_entry(sv):
@@ -109,17 +110,18 @@ def test_full_size_sampled_rows(sv, wl_name):
 
 
 @pytest.mark.parametrize("wl_name", ["headline", "p1440"])
-def test_full_size_sampled_rows_blocked_order(sv, wl_name):
-    """The full-size workloads with their temporal heads in the blocked
-    temporal-major order, in the benchmark's launch configuration."""
+@pytest.mark.parametrize("order", ["tmb", "tms"])
+def test_full_size_sampled_rows_blocked_order(sv, wl_name, order):
+    """The full-size workloads with their temporal heads in the blocked or
+    strip temporal-major order, in the benchmark's launch configuration."""
     wl = synth.WORKLOADS[wl_name]
     inp = synth.make_inputs(wl)
     rows = synth.sample_rows(wl, min(wl.sample_rows, 256))
-    orders = ["tmb" if h.kind == synth.TEMPORAL else h.order for h in wl.heads]
+    orders = [order if h.kind == synth.TEMPORAL else h.order for h in wl.heads]
     o = _run_layer(sv, wl, inp, 256, 64, orders=orders)
     ref = _oracle_rows(wl, inp, rows)
     got = np.stack([f64_of(o[h][torch.from_numpy(rows[h]).cuda()]) for h in range(wl.n_heads)])
-    assert_close(got, np.stack([r[0] for r in ref]), f"{wl_name} blocked order sampled rows")
+    assert_close(got, np.stack([r[0] for r in ref]), f"{wl_name} {order} order sampled rows")
 
 
 def test_perm_study_frame_major_order(sv):
@@ -196,13 +198,15 @@ def test_edge_geometries(sv, geom, heads, bq, bk):
     ((2, 3, 5), [synth.Head("dense"), synth.Head("temporal", radius=3, order="tm")]),
     ((5, 9, 11), [synth.Head("spatial", window=0), synth.Head("temporal", radius=1, order="tm")]),
     ((17, 6, 8), [synth.Head("temporal", radius=2, order="tmb"), synth.Head("spatial", window=1)]),
+    ((17, 6, 9), [synth.Head("temporal", radius=2, order="tms"), synth.Head("spatial", window=1)]),
 ])
 def test_d128_two_tiles_per_barrier(sv, geom, heads):
     """The head_dim 128, 256 x 64 launch runs two list entries between barriers.
     These geometries give lists of 1, 3, 5, 7, 8, 12 and 13 entries (so groups
     whose second entry is missing), ragged k- and q-tiles, patch runs shorter
-    than 16 keys (per-score test) and runs of exactly 16 in the blocked order;
-    every output row is checked against the oracle."""
+    than 16 keys (per-score test) and runs of exactly 16 in the blocked and
+    strip orders (with an odd grid width: a last strip one patch wide); every
+    output row is checked against the oracle."""
     F, H, W = geom
     wl = synth.Workload(name="tpb", seed=79, frames=F, height=H, width=W, head_dim=128,
                         heads=tuple(heads), tiles=((256, 64),))
@@ -236,7 +240,7 @@ def test_tiny_128_key_tiles_all_orders(sv):
     the oracle."""
     wl = synth.WORKLOADS["tiny"]
     inp = synth.make_inputs(wl)
-    for order in ("fm", "tm", "tmb"):
+    for order in ("fm", "tm", "tmb", "tms"):
         o = _run_layer(sv, wl, inp, 256, 128, orders=["fm", order])
         ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
         for h in range(wl.n_heads):
@@ -381,6 +385,9 @@ def test_persistent_schedule_over_several_launches(sv):
     ((21, 4, 6), 1, "tmb", 256, 64),  # blocked patch order: 4x4 and 4x2 blocks
     ((17, 9, 13), 2, "tmb", 128, 64), # ragged blocks in both directions, F-1 = 16
     ((21, 5, 7), 1, "tmb", 64, 32),
+    ((21, 4, 6), 1, "tms", 256, 64),  # snake strips: three strips of 2 columns
+    ((17, 9, 13), 2, "tms", 128, 64), # odd width: a last strip one patch wide, F-1 = 16
+    ((21, 5, 7), 1, "tms", 64, 32),
 ])
 def test_long_run_masks_all_rows(sv, geom, r, order, bq, bk):
     """Geometries whose key runs (F-1 frames of a patch in temporal-major order,
@@ -418,7 +425,8 @@ def test_tile_aligned_long_runs(sv):
     """Tile snapping with key runs of 20 frames (the headline's F - 1) and a
     ragged tail, temporal-major and frame-major temporal heads."""
     heads = (synth.Head("temporal", radius=1, order="tm"), synth.Head("temporal", radius=2, order="fm"),
-             synth.Head("spatial", window=1), synth.Head("temporal", radius=1, order="tmb"))
+             synth.Head("spatial", window=1), synth.Head("temporal", radius=1, order="tmb"),
+             synth.Head("temporal", radius=1, order="tms"))
     wl = synth.Workload(name="ta", seed=29, frames=21, height=4, width=6, head_dim=128, heads=heads,
                         tiles=((128, 64),))
     inp = synth.make_inputs(wl)
@@ -449,15 +457,17 @@ def test_fused_permutation_bit_identical(sv, wl_name, bq, bk, persistent):
     assert (bits_of(o_sep) == bits_of(o_fused)).all()
 
 
-@pytest.mark.parametrize("geom,bq,bk,second", [((4, 8, 8), 256, 64, "tmb"), ((5, 24, 40), 128, 64, "tmb"),
-                                               ((17, 9, 13), 64, 32, "tmb"), ((5, 24, 40), 256, 64, "tm"),
-                                               ((21, 9, 14), 256, 64, "tm")])
-def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk, second):
+@pytest.mark.parametrize("geom,bq,bk,first,second", [
+    ((4, 8, 8), 256, 64, "tmb", "tmb"), ((5, 24, 40), 128, 64, "tmb", "tmb"), ((17, 9, 13), 64, 32, "tmb", "tmb"),
+    ((5, 24, 40), 256, 64, "tmb", "tm"), ((21, 9, 14), 256, 64, "tmb", "tm"),
+    ((4, 8, 8), 256, 64, "tms", "tms"), ((17, 9, 13), 64, 32, "tms", "tms"), ((21, 9, 13), 256, 64, "tms", "tmb"),
+    ((5, 24, 40), 128, 64, "tms", "tm")])
+def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk, first, second):
     """Fused and separate paths agree bit for bit with temporal heads in the
-    blocked order (and, second = "tm", a head of the raster temporal-major
-    order in the same call); both within the bar of the oracle."""
+    blocked or strip order (and a second temporal head of another
+    temporal-major order in the same call); both within the bar of the oracle."""
     from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
-    heads = (synth.Head("spatial", window=1), synth.Head("temporal", radius=2, order="tmb"),
+    heads = (synth.Head("spatial", window=1), synth.Head("temporal", radius=2, order=first),
              synth.Head("temporal", radius=1, order=second))
     F, H, W = geom
     wl = synth.Workload(name="fb", seed=37, frames=F, height=H, width=W, head_dim=128, heads=heads,
@@ -473,7 +483,7 @@ def test_fused_permutation_blocked_order_bit_identical(sv, geom, bq, bk, second)
     assert (bits_of(o_sep) == bits_of(o_fused)).all()
     ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * len(heads))
     for h in range(len(heads)):
-        assert_close(f64_of(o_fused[h]), ref[h][0], f"fused tmb/{second} {geom} h{h}")
+        assert_close(f64_of(o_fused[h]), ref[h][0], f"fused {first}/{second} {geom} h{h}")
 
 
 def test_fused_permutation_lse_and_ragged_long_runs(sv):

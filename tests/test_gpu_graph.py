@@ -41,12 +41,12 @@ def _capture(fn):
 def test_layer_step_replays_bit_identical(sv, fused):
     """permute -> persistent forward (work-counter clear kernel included) ->
     unpermute, or the fused forward, on the 4,800-token workload with the
-    temporal heads in the blocked temporal-major order."""
+    temporal heads in the strip temporal-major order."""
     from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
     wl = synth.WORKLOADS["small"]
     inp = synth.make_inputs(wl)
     g = sv.Geom(wl.frames, wl.height, wl.width)
-    masks = [sv_mask(h, "tmb" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
+    masks = [sv_mask(h, "tms" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
     layer = SparseVideoAttention(g, masks, wl.head_dim, 256, 64, fused=fused)
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
     scales = [float(s) for s in inp.scales]

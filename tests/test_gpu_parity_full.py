@@ -131,22 +131,25 @@ def _run_case(sv, wl_name, temporal_order, heads, per_tile, check_lse):
         assert lse_err <= LSE_TOL, lse_err
 
 
-@pytest.mark.parametrize("order", ["tmb", "tm"])
+@pytest.mark.parametrize("order", ["tms", "tmb", "tm"])
 def test_headline_every_qtile(sv, order):
-    """75,600 tokens x 10 heads (5 spatial, 5 temporal), both temporal-major orders."""
+    """75,600 tokens x 10 heads (5 spatial, 5 temporal), the three temporal-major orders."""
     _run_case(sv, "headline", order, list(range(10)), per_tile=3, check_lse=True)
 
 
-def test_ten_temporal_heads_every_qtile(sv):
-    """75,600 tokens, ten temporal heads (radius 22), blocked temporal-major order."""
-    _run_case(sv, "perm_study", "tmb", list(range(10)), per_tile=3, check_lse=True)
+@pytest.mark.parametrize("order", ["tms", "tmb"])
+def test_ten_temporal_heads_every_qtile(sv, order):
+    """75,600 tokens, ten temporal heads (radius 22), strip and blocked temporal-major orders."""
+    _run_case(sv, "perm_study", order, list(range(10)), per_tile=3, check_lse=True)
 
 
-@pytest.mark.parametrize("heads", [[0, 1], [2, 3], [4, 5], [6, 7], [8, 9]])
-def test_p1440_every_qtile(sv, heads):
+@pytest.mark.parametrize("heads,order", [([0, 1], "tms"), ([2, 3], "tms"), ([4, 5], "tms"), ([6, 7], "tms"),
+                                         ([8, 9], "tms"), ([5, 6], "tmb")])
+def test_p1440_every_qtile(sv, heads, order):
     """302,400 tokens x 10 heads: one row per q-tile (1,182 per head) plus the
-    last row, split over five tests to bound each one's oracle time."""
-    _run_case(sv, "p1440", "tmb", heads, per_tile=1, check_lse=True)
+    last row, split over five tests to bound each one's oracle time (and two
+    temporal heads in the blocked order)."""
+    _run_case(sv, "p1440", order, heads, per_tile=1, check_lse=True)
 
 
 def test_headline_routing_against_oracle(sv):
@@ -196,7 +199,7 @@ def test_headline_fused_step_bit_identical(sv):
     wl = synth.WORKLOADS["headline"]
     inp = _inputs("headline")
     g = sv.Geom(wl.frames, wl.height, wl.width)
-    masks = [sv_mask(h, "tmb" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
+    masks = [sv_mask(h, "tms" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
     scales = [float(s) for s in inp.scales]
     o_sep = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK)(q, k, v, scales)
@@ -208,7 +211,7 @@ def test_headline_fused_step_bit_identical(sv):
 def test_headline_tile_aligned_sampled_qtiles(sv):
     """The tile-aligned traversal at full size in the benchmark's launch
     configuration (256 x 64 maps built with MAP_TILE_ALIGNED, temporal heads in
-    the blocked order): for each head, twelve q-tiles (the first, the ragged
+    the strip order): for each head, twelve q-tiles (the first, the ragged
     last and ten seeded ones) and three rows in each against the oracle's
     tile-snapped mask."""
     from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
@@ -216,7 +219,7 @@ def test_headline_tile_aligned_sampled_qtiles(sv):
     inp = _inputs("headline")
     g = sv.Geom(wl.frames, wl.height, wl.width)
     og = oracle.Geometry(wl.frames, wl.height, wl.width)
-    orders = ["tmb" if h.kind == synth.TEMPORAL else "fm" for h in wl.heads]
+    orders = ["tms" if h.kind == synth.TEMPORAL else "fm" for h in wl.heads]
     masks = [sv_mask(h, o) for h, o in zip(wl.heads, orders)]
     layer = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK, map_flags=sv.MAP_TILE_ALIGNED)
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
@@ -248,7 +251,7 @@ def test_headline_tile_aligned_sampled_qtiles(sv):
         refs = list(ex.map(oracle_head, jobs))
     got = np.concatenate([f64_of(out[h][torch.from_numpy(tok).cuda()]) for h, tok in jobs])
     want = np.concatenate(refs)
-    _report("headline/tile-aligned/tmb/12-qtiles-per-head", got, want, None)
+    _report("headline/tile-aligned/tms/12-qtiles-per-head", got, want, None)
     assert_close(got, want, "headline tile-aligned")
 
 
@@ -266,7 +269,7 @@ def test_headline_dense_and_naive_comparators(sv):
     scales = [float(s) for s in inp.scales]
     dense = SparseVideoAttention(g, [sv.Mask(sv.DENSE, sv.FRAME_MAJOR, 0, 0)] * wl.n_heads, wl.head_dim, BQ, BK)
     o_dense = dense(q, k, v, scales)
-    masks = [sv_mask(h, "tmb" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
+    masks = [sv_mask(h, "tms" if h.kind == synth.TEMPORAL else "fm") for h in wl.heads]
     o_exact = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK)(q, k, v, scales)
     o_naive = SparseVideoAttention(g, masks, wl.head_dim, BQ, BK, map_flags=sv.MAP_ALL_BOUNDARY)(q, k, v, scales)
     torch.cuda.synchronize()

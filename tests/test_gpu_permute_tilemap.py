@@ -19,11 +19,14 @@ def sv():
     return m
 
 
-@pytest.mark.parametrize("order", ["tm", "tmb"])
+ORDER_CODE = {"tm": 1, "tmb": 2, "tms": 3}  # SVATTN_TEMPORAL_MAJOR / _BLOCKED / _STRIPS
+
+
+@pytest.mark.parametrize("order", ["tm", "tmb", "tms"])
 @pytest.mark.parametrize("F,H,W", GEOMS + [(3, 9, 13), (4, 13, 17)])
 def test_permutation_index_bit_exact(sv, F, H, W, order):
     g = sv.Geom(F, H, W)
-    perm, inv = sv.permutation_index(g, order=sv.TEMPORAL_MAJOR if order == "tm" else sv.TEMPORAL_MAJOR_BLOCKED)
+    perm, inv = sv.permutation_index(g, order=ORDER_CODE[order])
     ref = oracle.layout_tokens(oracle.Geometry(F, H, W), order)
     p = perm.cpu().numpy()
     assert (p == ref).all()
@@ -31,7 +34,7 @@ def test_permutation_index_bit_exact(sv, F, H, W, order):
     assert (iv[ref] == np.arange(g.n)).all()
 
 
-@pytest.mark.parametrize("order", ["tm", "tmb"])
+@pytest.mark.parametrize("order", ["tm", "tmb", "tms"])
 @pytest.mark.parametrize("F,H,W,d,heads", [(4, 8, 8, 64, 2), (5, 24, 40, 128, 3), (3, 5, 7, 128, 2),
                                            (21, 45, 80, 128, 5), (1, 4, 4, 64, 1), (3, 9, 13, 64, 2)])
 def test_permute_unpermute_bit_exact(sv, F, H, W, d, heads, order):
@@ -39,7 +42,7 @@ def test_permute_unpermute_bit_exact(sv, F, H, W, d, heads, order):
     x = synth.random_bf16((heads, g.n, d), seed=F * 1000 + W)
     xd = to_dev(x)
     perm = oracle.layout_tokens(oracle.Geometry(F, H, W), order)
-    o = sv.TEMPORAL_MAJOR if order == "tm" else sv.TEMPORAL_MAJOR_BLOCKED
+    o = ORDER_CODE[order]
     y = sv.permute_tokens(g, xd, order=o)
     torch.cuda.synchronize()
     assert (bits_of(y) == x[:, perm]).all()
@@ -99,6 +102,12 @@ SMALL_CASES = (
                        ((1, 4, 4), 1), ((4, 13, 17), 5)]
        for bq, bk in [(32, 32), (128, 64), (256, 64)]]
     + [((4, 8, 8), "dense", 0, 0, "tmb", 64, 64)]
+    # temporal-major over snake strips, odd widths (a last strip one patch wide) included
+    + [(geom, "temporal", 0, r, "tms", bq, bk)
+       for geom, r in [((4, 8, 8), 1), ((5, 24, 40), 2), ((3, 9, 13), 2), ((3, 5, 7), 1), ((7, 1, 9), 2),
+                       ((1, 4, 4), 1), ((4, 13, 17), 5)]
+       for bq, bk in [(32, 32), (128, 64), (256, 64)]]
+    + [((4, 8, 8), "dense", 0, 0, "tms", 64, 64)]
 )
 
 
@@ -115,7 +124,9 @@ def test_tile_map_bit_exact(sv, geom, kind, w, r, order, bq, bk):
 @pytest.mark.parametrize("wl_name,hi,order", [("headline", 0, "fm"), ("headline", 5, "tm"),
                                               ("headline", 5, "fm"), ("perm_study", 0, "tm"),
                                               ("p1440", 0, "fm"), ("p1440", 5, "tm"), ("headline", 5, "tmb"),
-                                              ("perm_study", 0, "tmb"), ("p1440", 5, "tmb")])
+                                              ("perm_study", 0, "tmb"), ("p1440", 5, "tmb"),
+                                              ("headline", 5, "tms"), ("perm_study", 0, "tms"),
+                                              ("p1440", 5, "tms")])
 @pytest.mark.parametrize("bq,bk", [(256, 64), (128, 32)])
 def test_tile_map_large_sampled_rows(sv, wl_name, hi, order, bq, bk):
     wl = synth.WORKLOADS[wl_name]
@@ -151,7 +162,8 @@ def _oracle_map_threaded(geom, kind, w, r, order, bq, bk):
 
 
 @pytest.mark.parametrize("wl_name,hi,order", [("headline", 0, "fm"), ("headline", 5, "tm"),
-                                              ("headline", 5, "tmb"), ("perm_study", 0, "tmb")])
+                                              ("headline", 5, "tmb"), ("perm_study", 0, "tmb"),
+                                              ("headline", 5, "tms"), ("perm_study", 0, "tms")])
 def test_tile_map_full_size_every_row(sv, wl_name, hi, order):
     """The benchmark's 256 x 64 maps at 75,600 tokens, whole: every q-tile row's
     classes, CSR list and the longest-first q-tile order, bit for bit."""

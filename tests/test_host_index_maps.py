@@ -20,7 +20,7 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "tests", "host", "index_check.cpp")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
-ORDERS = {"fm": 0, "tm": 1, "tmb": 2}
+ORDERS = {"fm": 0, "tm": 1, "tmb": 2, "tms": 3}
 KINDS = {"spatial": 0, "temporal": 1, "dense": 2}
 
 
@@ -46,7 +46,7 @@ GEOMS = [(3, 5, 6), (4, 8, 8), (5, 24, 40), (21, 45, 80), (2, 3, 5), (1, 4, 4), 
          (3, 7, 1), (4, 13, 17), (2, 90, 160)]
 
 
-@pytest.mark.parametrize("order", ["tm", "tmb"])
+@pytest.mark.parametrize("order", ["tm", "tmb", "tms"])
 @pytest.mark.parametrize("F,H,W", GEOMS)
 def test_permutation_maps_match_oracle(exe, F, H, W, order):
     g = oracle.Geometry(F, H, W)
@@ -59,15 +59,17 @@ def test_permutation_maps_match_oracle(exe, F, H, W, order):
 
 
 CLASS_CASES = (
-    [((F, H, W), "temporal", 0, r, "tmb", bq, bk)
+    [((F, H, W), "temporal", 0, r, order, bq, bk)
+     for order in ("tmb", "tms")
      for (F, H, W) in [(3, 5, 6), (4, 8, 8), (3, 9, 13), (2, 3, 5), (4, 13, 17), (3, 7, 1), (2, 1, 7)]
      for r in (0, 1, 2, 5)
      for bq, bk in [(32, 32), (64, 32), (32, 64), (128, 64), (256, 64)]]
-    + [((5, 24, 40), "temporal", 0, r, "tmb", bq, bk) for r in (1, 3) for bq, bk in [(128, 64), (256, 64)]]
+    + [((5, 24, 40), "temporal", 0, r, order, bq, bk) for order in ("tmb", "tms") for r in (1, 3)
+       for bq, bk in [(128, 64), (256, 64)]]
     + [((F, H, W), kind, w, r, order, bq, bk)
        for (F, H, W) in [(3, 5, 6), (4, 8, 8), (3, 9, 13)]
        for kind, w, r, order in [("temporal", 0, 1, "tm"), ("temporal", 0, 2, "fm"), ("spatial", 1, 0, "fm"),
-                                 ("dense", 0, 0, "tmb")]
+                                 ("dense", 0, 0, "tmb"), ("dense", 0, 0, "tms")]
        for bq, bk in [(32, 32), (128, 64)]]
 )
 
@@ -101,8 +103,11 @@ FULL_SIZE_MAPS = [
     ((21, 45, 80), "temporal", 0, 31, "tm", None),
     ((21, 45, 80), "temporal", 0, 31, "tmb", None),
     ((21, 45, 80), "temporal", 0, 22, "tmb", None),
+    ((21, 45, 80), "temporal", 0, 31, "tms", None),
+    ((21, 45, 80), "temporal", 0, 22, "tms", None),
     ((21, 90, 160), "spatial", 1, 0, "fm", 16),
     ((21, 90, 160), "temporal", 0, 62, "tmb", 16),
+    ((21, 90, 160), "temporal", 0, 62, "tms", 16),
 ]
 
 

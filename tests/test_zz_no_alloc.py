@@ -50,7 +50,7 @@ def _both(sv, g, masks, mp, q, k, v, scales):
 
 def test_noalloc_matches_workspace_entry_two_calls(sv):
     big = synth.WORKLOADS["headline"]
-    orders = ["tmb" if h.kind == synth.TEMPORAL else "fm" for h in big.heads]
+    orders = ["tms" if h.kind == synth.TEMPORAL else "fm" for h in big.heads]
     print("call 1: 75,600 tokens x 10 heads", flush=True)
     g, masks, mp, _, q, k, v, scales = _case(sv, big, orders)
     _both(sv, g, masks, mp, q, k, v, scales)
