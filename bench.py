@@ -58,16 +58,18 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, temporal_order: str):
     """HBM bytes per forward launch from the committed counter summary, or None
-    when there is none for this workload or the kernel sources changed since."""
+    when there is none for this workload and token order or the kernel sources
+    changed since."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             text = f.read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("sources_sha256") != kernel_sources_sha256():
+    if rec.get("workload") != workload or rec.get("temporal_order") != temporal_order or \
+            rec.get("sources_sha256") != kernel_sources_sha256():
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -370,7 +372,7 @@ def main():
         sclk = clock_under_load(lambda: layer.attend(q, k, v, out, scales))
         log(f"graphics clock under load: {sclk}")
 
-    traffic = measured_traffic(wl.name) if args.block_q == 256 and args.block_k == 64 else None
+    traffic = measured_traffic(wl.name, args.temporal_order) if args.block_q == 256 and args.block_k == 64 else None
     log(f"traffic per forward launch (committed counters): {traffic}")
 
     result = {
