@@ -271,9 +271,11 @@ def test_traffic_summary_parses():
     assert len(rec["sources_sha256"]) == 64
     sys.path.insert(0, root)
     import bench
-    t = bench.measured_traffic("headline")
+    t = bench.measured_traffic("headline", rec["temporal_order"])
     assert t is None or t == rec["traffic_bytes_per_launch"]
-    assert bench.measured_traffic("small") is None
+    assert bench.measured_traffic("small", rec["temporal_order"]) is None
+    other = "tmb" if rec["temporal_order"] != "tmb" else "tms"
+    assert bench.measured_traffic("headline", other) is None          # counters of another token order
 
 
 def test_forward_fused_validation():
