@@ -376,6 +376,19 @@ static int run_launches(FwdArgs base, const std::vector<HeadDesc>& descs, int he
     a.n_slots = nh;
     if (a.n_split < 1) a.n_split = 1;
     a.n_items = nh * a.n_sel * a.n_split;
+    // Heads run one after another (each longest row first), which keeps one head's K/V in an XCD's L2 at a
+    // time.  When every head of the launch shares one map, the last head's longest rows would start only in
+    // the last stretch of the launch and leave most workgroups idle at its end, so the last kTailHeads heads
+    // are dealt rank by rank instead.  (Heads come heaviest mask first, so in a launch of several maps the
+    // last map's rows are the shortest and already fill the end.)
+    a.tail_m = 0;
+    if (a.queue && !a.use_sel && a.n_split == 1 && !a.dense_bits && nh >= 2) {
+      bool one_map = true;
+      for (int i = 0; i + 1 < nh; ++i)
+        one_map = one_map && a.heads[i].row_ptr == a.heads[nh - 1].row_ptr &&
+                  a.heads[i].qt_order == a.heads[nh - 1].qt_order;
+      if (one_map) a.tail_m = std::min(nh, kTailHeads);
+    }
     if (a.queue) {
       // launches on one stream run in order, so one counter serves them all
       hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, st, a.queue);

@@ -201,10 +201,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   while (item < a.n_items) {
   const int per_slot = a.n_sel * a.n_split;
-  const int slot = item / per_slot;
-  const int rest = item - slot * per_slot;
-  const int sel = a.n_split == 1 ? rest : rest / a.n_split;  // rank of the q-tile among the head's work items
-  const int split = rest - sel * a.n_split;                  // key split of the item
+  const int tail0 = a.n_items - a.tail_m * a.n_sel;  // first item of the rank-by-rank tail (tail_m > 1)
+  int slot, sel, split;  // head slot, rank of the q-tile among the head's work items, key split
+  if (a.tail_m > 1 && item >= tail0) {
+    const int r = item - tail0;
+    sel = r / a.tail_m;
+    slot = a.n_slots - a.tail_m + (r - sel * a.tail_m);
+    split = 0;
+  } else {
+    slot = item / per_slot;
+    const int rest = item - slot * per_slot;
+    sel = a.n_split == 1 ? rest : rest / a.n_split;
+    split = rest - sel * a.n_split;
+  }
   const HeadDesc& hd = a.heads[slot];
   const int qt = a.use_sel ? a.qt_sel[sel] : (BITS || !hd.qt_order) ? sel : ld_const(hd.qt_order + sel);
   const Geo g = a.g;

@@ -222,6 +222,7 @@ constexpr int kNoallocScratchBytes = 256;
 static_assert(kNoallocScratchBytes >= SVATTN_FORWARD_WORKSPACE_BYTES, "forward workspace must fit the scratch area");
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSelectedTiles = 32;  // q-tiles of a selected-rows launch (kernel arguments)
+constexpr int kTailHeads = 3;          // most head slots dealt rank by rank at the end of a launch
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 struct FwdArgs {
@@ -238,6 +239,9 @@ struct FwdArgs {
   // takes the map entries whose keys lie in 128-key units [s U / n_split, (s + 1) U / n_split), U =
   // ceil(N / 128), so a split covers the same keys whatever the map's block_k.
   int32_t n_split;
+  // > 1 (persistent whole-row launches whose heads all share one tile map): the last tail_m head slots are
+  // dealt rank by rank at the end of the work order (rank-0 q-tiles of all of them, then rank 1, ...)
+  int32_t tail_m;
   // 1: O is fp32, normalised over the split's keys alone, with lse of the split (-inf when it keeps no
   // key); rows of (selected q-tile i, split s) at (i * n_split + s) * block_q + row
   int32_t partial;

@@ -30,6 +30,14 @@ void check_fwd(const FwdArgs& a, int block_q, int block_k) {
   }
   // key splits and partial outputs only for selected whole q-tiles
   if ((a.n_split > 1 || a.partial) && (!a.use_sel || !a.compact || !a.partial)) abort();
+  // rank-by-rank tail: persistent whole-row launches only, over trailing heads of one map
+  if (a.tail_m < 0 || a.tail_m == 1 || a.tail_m > kTailHeads || a.tail_m > a.n_slots) abort();
+  if (a.tail_m > 1) {
+    if (!a.queue || a.use_sel || a.n_split != 1 || a.dense_bits) abort();
+    const HeadDesc& last = a.heads[a.n_slots - 1];
+    for (int i = a.n_slots - a.tail_m; i < a.n_slots; ++i)
+      if (a.heads[i].row_ptr != last.row_ptr || a.heads[i].qt_order != last.qt_order) abort();
+  }
   if (block_q < 32 || block_k < 32 || a.n_qt < 1 || a.n_kt < 1) abort();
   for (int i = 0; i < a.n_slots; ++i) {
     const HeadDesc& h = a.heads[i];
