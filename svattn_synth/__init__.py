@@ -104,6 +104,12 @@ WORKLOADS = {
         heads=tuple([Head(TEMPORAL, radius=22, order=TEMPORAL_MAJOR)] * 10),
         tiles=((256, 64),), sample_rows=128, sample_seed=13,
         description="75,600 tokens, 10 temporal heads r=22, frame-major vs temporal-major"),
+    "headline_alt": Workload(
+        name="headline_alt", seed=6, frames=21, height=45, width=80, head_dim=128,
+        heads=_mix(5, 7, 5, 11),
+        tiles=((256, 64),), random_scale=True, sample_rows=256, sample_seed=14,
+        description="the headline's 75,600 tokens with the other mask fit of its density: 5 spatial w=7 + "
+                    "5 temporal r=11 (38.887% kept), d=128, per-head softmax-scale multiplier in [0.5, 2]"),
     "p1440": Workload(
         name="p1440", seed=4, frames=21, height=90, width=160, head_dim=128,
         heads=_mix(5, 1, 5, 62),

@@ -137,6 +137,12 @@ def test_headline_every_qtile(sv, order):
     _run_case(sv, "headline", order, list(range(10)), per_tile=3, check_lse=True)
 
 
+def test_headline_alternative_fit_every_qtile(sv):
+    """75,600 tokens x 10 heads with the other mask fit of the same density
+    (5 spatial w=7 + 5 temporal r=11), temporal heads in the strip order."""
+    _run_case(sv, "headline_alt", "tms", list(range(10)), per_tile=3, check_lse=True)
+
+
 @pytest.mark.parametrize("order", ["tms", "tmb"])
 def test_ten_temporal_heads_every_qtile(sv, order):
     """75,600 tokens, ten temporal heads (radius 22), strip and blocked temporal-major orders."""

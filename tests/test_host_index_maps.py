@@ -105,6 +105,8 @@ FULL_SIZE_MAPS = [
     ((21, 45, 80), "temporal", 0, 22, "tmb", None),
     ((21, 45, 80), "temporal", 0, 31, "tms", None),
     ((21, 45, 80), "temporal", 0, 22, "tms", None),
+    ((21, 45, 80), "temporal", 0, 11, "tms", None),
+    ((21, 45, 80), "spatial", 7, 0, "fm", 8),
     ((21, 90, 160), "spatial", 1, 0, "fm", 16),
     ((21, 90, 160), "temporal", 0, 62, "tmb", 16),
     ((21, 90, 160), "temporal", 0, 62, "tms", 16),

@@ -115,6 +115,28 @@ def test_headline_density_matches_pages():
     assert list(got_t) == [_row_closed_temporal(F, H, W, 31, int(t)) for t in rows]
 
 
+def test_alternative_fit_density_matches_pages():
+    """The other mask fit of the pages' ~38.87% (w=7 on 5 spatial heads, r=11
+    on 5 temporal heads; closer to the pages' "small region" wording for
+    temporal heads, further from "nearby frames" for spatial ones) is within
+    0.02 points of it; the oracle's per-row counts agree with the closed form."""
+    pages = _golden("pages_numbers.json")
+    target = pages["kept_fraction_percent"]["value"]
+    wl = synth.WORKLOADS["headline_alt"]
+    F, H, W = wl.frames, wl.height, wl.width
+    N = F * H * W
+    kept = sum(_closed_spatial(F, H, W, h.window) if h.kind == "spatial"
+               else _closed_temporal(F, H, W, h.radius) for h in wl.heads)
+    pct = 100.0 * kept / (wl.n_heads * N * N)
+    assert abs(pct - target) < 0.02, pct
+    g = Geometry(F, H, W)
+    rows = synth.sample_rows(wl, 32)[0]
+    got_s = oracle.kept_counts_per_row(g, "spatial", 7, 0, rows)
+    got_t = oracle.kept_counts_per_row(g, "temporal", 0, 11, rows)
+    assert list(got_s) == [_row_closed_spatial(F, H, W, 7, int(t)) for t in rows]
+    assert list(got_t) == [_row_closed_temporal(F, H, W, 11, int(t)) for t in rows]
+
+
 def test_mask_hand_examples():
     ex = _golden("tiny_hand_examples.json")
     g = Geometry(**ex["geometry"])
