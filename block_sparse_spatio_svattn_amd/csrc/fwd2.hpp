@@ -159,6 +159,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int STAGES = PP ? 3 : 2 * TPB;
   __shared__ __attribute__((aligned(16))) char smem[STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int kcs[STAGES][BK];
+  // Gathered heads, plain schedule: the frame-major rows of the keys of the
+  // tiles 2 TPB list steps ahead, one slot per tile, written by one wave.
+  __shared__ int grow[GTH && !PP ? 2 * TPB : 1][BK];
 
   __shared__ int ticket;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -400,7 +403,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // form per lane and tile instead of one per copy.
   // The offsets are worked out when the tile's turn in the list comes, one
   // step before its copies go out, so the cross-lane reads land while the
-  // wave computes scores.
+  // wave computes scores.  (In the plain schedule only an item's first TPB
+  // tiles are done this way; later tiles take their rows from a ring in LDS
+  // that one wave fills per tile, see the main loop.)
   static_assert(BK <= 64, "one lane per key of a tile");
   const bool gathered = GTH && hd.gather;
   uint32_t goff[GTH ? OPC : 1];  // this lane's copy offsets for the next gathered tile
@@ -848,15 +853,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // before the last barrier; the wave has no LDS reads in flight here),
     // then P V; one barrier ends the group.
     // Tile list window: wk/wc[0] is the current tile, [TPB] the one whose
-    // copies go out with it, [TPB + 1] fetched ahead.
-    int wk[TPB + 2], wc[TPB + 2];
+    // copies go out with it, [LA] fetched ahead (gathered heads also use
+    // [2 TPB], the tile whose rows go into the row ring).
+    //
+    // Gathered heads: the rows of a tile's keys are a closed form that every
+    // wave would otherwise work out for every tile; here the rows of tile
+    // t + 2 TPB are worked out once, by wave t % NW while the group of tile t
+    // runs, into slot (t + 2 TPB) % 2 TPB of `grow`, and read back by every
+    // wave with its copies' offsets one group later (a barrier in between).
+    // A slot is rewritten 2 TPB tiles after it was written, always in a later
+    // group than its readers.  The first 2 TPB tiles: the first TPB work out
+    // their own offsets, the next TPB go into the ring before the first
+    // barrier.
+    constexpr int LA = GTH ? 2 * TPB + 1 : TPB + 1;
+    int wk[LA + 1], wc[LA + 1];
 #pragma unroll
-    for (int i = 0; i < TPB + 2; ++i) {
+    for (int i = 0; i <= LA; ++i) {
       wk[i] = 0;
       wc[i] = 0;
     }
 #pragma unroll
-    for (int i = 0; i <= TPB; ++i) fetch(i, wk[i], wc[i]);
+    for (int i = 0; i < LA; ++i) fetch(i, wk[i], wc[i]);
+    auto ring_write = [&](int t, int key0) __attribute__((always_inline)) {
+      if constexpr (GTH) {
+        if (wave_u == t % NW && lane < BK) grow[t % (2 * TPB)][lane] = tm_to_fm(g, order, min(key0 + lane, N - 1));
+      }
+    };
+    auto ring_offsets = [&](int t) __attribute__((always_inline)) {
+      if constexpr (GTH) {
+#pragma unroll
+        for (int i = 0; i < OPC; ++i) {
+          const uint32_t off = (uint32_t)dma_off[i];
+          // (the clamp keeps a copy inside the tensor whatever the slot holds)
+          const uint32_t row = min((uint32_t)grow[t % (2 * TPB)][off / (D * 2)], (uint32_t)(N - 1));
+          goff[i] = row * (uint32_t)(D * 2) + off % (D * 2);
+        }
+      }
+    };
     if (n > 0) {
       if (gathered) gather_offsets(wk[0]);
       issue(wk[0], 0);
@@ -866,6 +899,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (gathered) gather_offsets(wk[1]);
         issue(wk[1], 1);
       }
+    if (gathered) {
+#pragma unroll
+      for (int t = TPB; t < 2 * TPB; ++t)
+        if (t < n) ring_write(t, wk[t]);
+    }
     wait_tiles();
     __syncthreads();
     int grp = 0;  // first stage of the current group
@@ -875,8 +913,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int t = j + u;
         if (u == 0 || t < n) {
           const int st = grp + u;
-          fetch(t + TPB + 1, wk[TPB + 1], wc[TPB + 1]);
-          if (gathered && t + TPB < n) gather_offsets(wk[TPB]);
+          fetch(t + LA, wk[LA], wc[LA]);
+          if (gathered) {
+            if (t + TPB < n) ring_offsets(t + TPB);
+            if (t + 2 * TPB < n) ring_write(t + 2 * TPB, wk[2 * TPB]);
+          }
           // a wave whose queries keep no key of this tile skips S, softmax and P V
           uint64_t keep[QG];
           const int ms = plan(st, wk[0], wc[0], keep);
@@ -893,7 +934,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           __builtin_amdgcn_sched_barrier(0);
           if (ms != 2) pv(st, P, [](int) {});
 #pragma unroll
-          for (int i = 0; i <= TPB; ++i) {
+          for (int i = 0; i < LA; ++i) {
             wk[i] = wk[i + 1];
             wc[i] = wc[i + 1];
           }
