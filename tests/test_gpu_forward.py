@@ -375,6 +375,31 @@ def test_persistent_schedule_over_several_launches(sv):
         assert_close(f64_of(o_p[h]), ref[h][0], f"many h{h}")
 
 
+@pytest.mark.parametrize("n_heads,d,bq,bk", [(2, 128, 256, 64), (5, 128, 256, 64), (20, 64, 64, 32), (3, 128, 128, 64)])
+def test_one_map_launch_rank_by_rank_tail(sv, n_heads, d, bq, bk):
+    """Heads that all share one tile map: the persistent schedule deals the
+    last (up to three) heads of each launch rank by rank.  Only which
+    workgroup runs an item changes, so the output equals the static grid's bit
+    for bit (2, 3 and 5 heads; 20 heads in two launches of 16 and 4) and the
+    oracle on every row."""
+    from block_sparse_spatio_svattn_amd.layer import SparseVideoAttention
+    heads = tuple([synth.Head("temporal", radius=2, order="tms")] * n_heads)
+    wl = synth.Workload(name="onemap", seed=41, frames=5, height=6, width=9, head_dim=d, heads=heads,
+                        tiles=((bq, bk),))
+    inp = synth.make_inputs(wl)
+    g = sv.Geom(wl.frames, wl.height, wl.width)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    scales = [float(s) for s in inp.scales]
+    masks = [sv_mask(h) for h in heads]
+    o_p = SparseVideoAttention(g, masks, d, bq, bk, persistent=True)(q, k, v, scales)
+    o_s = SparseVideoAttention(g, masks, d, bq, bk, persistent=False)(q, k, v, scales)
+    torch.cuda.synchronize()
+    assert (bits_of(o_p) == bits_of(o_s)).all()
+    ref = _oracle_rows(wl, inp, [np.arange(wl.n_tokens)] * wl.n_heads)
+    for h in range(wl.n_heads):
+        assert_close(f64_of(o_p[h]), ref[h][0], f"one map h{h} of {n_heads}")
+
+
 @pytest.mark.parametrize("geom,r,order,bq,bk", [
     ((17, 3, 5), 1, "tm", 64, 64),    # F-1 = 16: patch runs of 16 keys, ragged tail (N = 255)
     ((21, 4, 6), 1, "tm", 256, 64),   # F-1 = 20, as the headline; N = 504
