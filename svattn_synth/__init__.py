@@ -110,6 +110,12 @@ WORKLOADS = {
         tiles=((256, 64),), random_scale=True, sample_rows=256, sample_seed=14,
         description="the headline's 75,600 tokens with the other mask fit of its density: 5 spatial w=7 + "
                     "5 temporal r=11 (38.887% kept), d=128, per-head softmax-scale multiplier in [0.5, 2]"),
+    "headline_d64": Workload(
+        name="headline_d64", seed=7, frames=21, height=45, width=80, head_dim=64,
+        heads=_mix(2, 1, 2, 31),
+        tiles=((256, 64),), random_scale=True, sample_rows=256, sample_seed=15,
+        description="the headline's 75,600 tokens and masks at head_dim 64: 2 spatial w=1 + 2 temporal r=31 "
+                    "(a parity workload for the d64 kernels at full size)"),
     "p1440": Workload(
         name="p1440", seed=4, frames=21, height=90, width=160, head_dim=128,
         heads=_mix(5, 1, 5, 62),

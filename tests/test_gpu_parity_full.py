@@ -150,12 +150,19 @@ def test_ten_temporal_heads_every_qtile(sv, order):
 
 
 @pytest.mark.parametrize("heads,order", [([0, 1], "tms"), ([2, 3], "tms"), ([4, 5], "tms"), ([6, 7], "tms"),
-                                         ([8, 9], "tms"), ([5, 6], "tmb")])
+                                         ([8, 9], "tms"), ([5, 6], "tmb"), ([7, 8], "tm")])
 def test_p1440_every_qtile(sv, heads, order):
     """302,400 tokens x 10 heads: one row per q-tile (1,182 per head) plus the
     last row, split over five tests to bound each one's oracle time (and two
-    temporal heads in the blocked order)."""
+    temporal heads in each of the blocked and row-by-row orders)."""
     _run_case(sv, "p1440", order, heads, per_tile=1, check_lse=True)
+
+
+def test_headline_geometry_head_dim_64_every_qtile(sv):
+    """75,600 tokens at head_dim 64 (2 spatial w=1 + 2 temporal r=31, strip
+    order): the d64 kernels, which keep one tile per barrier, over every q-tile
+    of every head at full size."""
+    _run_case(sv, "headline_d64", "tms", [0, 1, 2, 3], per_tile=3, check_lse=True)
 
 
 def test_headline_routing_against_oracle(sv):
