@@ -101,7 +101,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs the kernel on one MI355X and has no "
+        print(f"bench.py measures one GPU: the library runs the kernel on one MI355X and has no "
               f"multi-GPU path (--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
 
